@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs for exact attention forward.
+
+This module holds the workload shapes and the seeded input generators, and
+nothing of the attention arithmetic itself.  Both the CPU oracle's tests and
+the GPU path's tests / benchmark draw their inputs from here, so the two
+sides always see bit-identical tensors.
+
+Inputs are i.i.d. standard normal, drawn on the CPU with a seeded
+``torch.Generator`` in float32 and then rounded to the I/O dtype (round to
+nearest even), so any host reproduces them exactly.  The pages measure only
+one real workload (GPT-2-medium attention: n = 1024, d = 64, 16 heads,
+batch 64; the "efficient attention" chapter, Dao et al. 2022 Fig. 2 table);
+the shapes below stand in for it and for the long-sequence cases the pages
+discuss, with synthetic values instead of a trained model's activations.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str            # "bf16" or "f32": the I/O element type
+    seed: int             # base seed: +0 Q, +1 K, +2 V, +3 outlier rows
+    k_outlier_frac: float = 0.0   # fraction of K rows (per (b, kv head)) scaled
+    k_outlier_scale: float = 1.0  # by this power of two (exact in bf16)
+    description: str = ""
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def shapes(self):
+        return ((self.B, self.Hq, self.N, self.d),
+                (self.B, self.Hkv, self.N, self.d))
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("single_head_n256_d64_f32", 1, 1, 1, 256, 64, "f32", 1000,
+                 description="single head, fp32 I/O, small enough for the oracle in seconds"),
+        Workload("gpt2_medium_b64_h16_n1024_d64", 64, 16, 16, 1024, 64, "bf16", 2000,
+                 description="GPT-2-medium-shaped attention forward"),
+        Workload("long_b4_h32_n4096_d128", 4, 32, 32, 4096, 128, "bf16", 3000,
+                 description="long-sequence attention forward (also run materialized)"),
+        Workload("gqa_b2_hq32_hkv8_n8192_d128", 2, 32, 8, 8192, 128, "bf16", 4000,
+                 description="grouped-query attention, 4 query heads per K/V head"),
+        Workload("gqa_b2_hq32_hkv8_n8192_d128_kscaled", 2, 32, 8, 8192, 128, "bf16", 4000,
+                 k_outlier_frac=0.01, k_outlier_scale=8.0,
+                 description="as above, 1% of K rows scaled by 8 to stress the running-max rescale"),
+        Workload("long_context_b1_h8_n32768_d128", 1, 8, 8, 32768, 128, "bf16", 5000,
+                 description="long-context attention forward; S+P would be 4.3 GB per head"),
+    ]
+}
+
+# The headline benchmark workload: the pages' one measured shape.
+DEFAULT_BENCH = "gpt2_medium_b64_h16_n1024_d64"
+
+
+def _randn(shape, seed: int) -> torch.Tensor:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+
+def outlier_rows(N: int, frac: float, seed: int, n_slices: int) -> list[torch.Tensor]:
+    """Row indices, per (b, kv head) slice, of the K rows to scale.
+
+    round(frac * N) distinct rows per slice, drawn without replacement by a
+    seeded permutation, one permutation per slice in (b, kv head) order.
+    """
+    count = int(round(frac * N))
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return [torch.randperm(N, generator=g)[:count] for _ in range(n_slices)]
+
+
+def make_inputs(w: Workload, *, B=None, Hq=None, Hkv=None, N=None, d=None,
+                dtype=None, seed=None):
+    """Seeded CPU tensors (q, k, v) for workload ``w`` (fields may be overridden).
+
+    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous, in the I/O dtype.
+    """
+    B = w.B if B is None else B
+    Hq = w.Hq if Hq is None else Hq
+    Hkv = w.Hkv if Hkv is None else Hkv
+    N = w.N if N is None else N
+    d = w.d if d is None else d
+    tdt = w.torch_dtype if dtype is None else dtype
+    seed = w.seed if seed is None else seed
+    q = _randn((B, Hq, N, d), seed + 0).to(tdt)
+    k = _randn((B, Hkv, N, d), seed + 1).to(tdt)
+    v = _randn((B, Hkv, N, d), seed + 2).to(tdt)
+    if w.k_outlier_frac > 0.0:
+        rows = outlier_rows(N, w.k_outlier_frac, seed + 3, B * Hkv)
+        kf = k.view(B * Hkv, N, d)
+        for s, idx in enumerate(rows):
+            # a power-of-two factor: exact in bf16 and fp32
+            kf[s, idx, :] = kf[s, idx, :] * w.k_outlier_scale
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def random_inputs(B, Hq, Hkv, N, d, dtype: torch.dtype, seed: int, std: float = 1.0):
+    """Seeded i.i.d. normal (q, k, v) of an arbitrary shape (for edge-case tests)."""
+    q = (_randn((B, Hq, N, d), seed + 0) * std).to(dtype).contiguous()
+    k = (_randn((B, Hkv, N, d), seed + 1) * std).to(dtype).contiguous()
+    v = (_randn((B, Hkv, N, d), seed + 2) * std).to(dtype).contiguous()
+    return q, k, v
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact upcast of a CPU/GPU tensor (bf16 or fp32) to a float64 NumPy array."""
+    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
