@@ -1,0 +1,167 @@
+"""Thin ctypes binding over libattn.so (include/attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the stream.
+There is no fallback: if the library is missing this module fails to import.
+
+Entry points carry the C names and take tensors instead of raw pointers:
+
+    attn_fwd(q, k, v, o, lse, scale, stream=None)                 bf16
+    attn_fwd_f32(q, k, v, o, lse, scale, stream=None)             fp32
+    attn_fwd_materialized(q, k, v, o, lse, s, p, scale, stream=None)
+    attn_fwd_materialized_f32(q, k, v, o, lse, s, p, scale, stream=None)
+    attn_strerror(status)
+
+plus ``fwd`` / ``fwd_materialized``, which allocate the outputs and pick the
+entry point by dtype.  q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous
+CUDA (HIP) tensors.  Argument errors raise ValueError, launch errors
+RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m exact_io_aware_73_amd.build` "
+        "(or __graft_entry__.build()) first.  There is no fallback path.")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_lib.attn_fwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]
+_lib.attn_fwd_f32.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]
+_lib.attn_fwd_materialized.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]
+_lib.attn_fwd_materialized_f32.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]
+for _fn in ("attn_fwd", "attn_fwd_f32", "attn_fwd_materialized", "attn_fwd_materialized_f32"):
+    getattr(_lib, _fn).restype = _I
+_lib.attn_strerror.argtypes = [_I]
+_lib.attn_strerror.restype = ctypes.c_char_p
+
+ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_GQA, ATTN_ERR_HEADDIM = 0, 1, 2, 3, 4
+ATTN_ERR_SCALE, ATTN_ERR_ALIGN, ATTN_ERR_ALIAS, ATTN_ERR_HIP = 5, 6, 7, 8
+
+
+def attn_strerror(status: int) -> str:
+    return _lib.attn_strerror(int(status)).decode()
+
+
+def _raise(status: int, fn: str):
+    if status == ATTN_OK:
+        return
+    msg = f"{fn}: {attn_strerror(status)} (status {status})"
+    if status == ATTN_ERR_HIP:
+        raise RuntimeError(msg)
+    raise ValueError(msg)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream))
+
+
+def _dims(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d], got {tuple(t.shape)}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k, v must be [B, Hkv, N, d] matching q {tuple(q.shape)}; "
+                         f"got {tuple(k.shape)} and {tuple(v.shape)}")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on one device")
+    return B, Hq, k.shape[1], N, d
+
+
+def _call(fn_name, dtype, q, k, v, o, lse, s, p, scale, stream):
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    for name, t, dt in (("q", q, dtype), ("k", k, dtype), ("v", v, dtype), ("o", o, dtype),
+                        ("lse", lse, torch.float32), ("s", s, torch.float32), ("p", p, dtype)):
+        if t is None:
+            continue
+        if t.dtype != dt:
+            raise ValueError(f"{fn_name}: {name} must be {dt}, got {t.dtype}")
+        if t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{fn_name}: {name} must be contiguous on {q.device}")
+    if o.shape != q.shape or lse.shape != (B, Hq, N):
+        raise ValueError(f"{fn_name}: o must be {tuple(q.shape)} and lse {(B, Hq, N)}")
+    for name, t in (("s", s), ("p", p)):
+        if t is not None and t.shape != (B, Hq, N, N):
+            raise ValueError(f"{fn_name}: {name} must be {(B, Hq, N, N)}")
+    fn = getattr(_lib, fn_name)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)]
+    if fn_name.startswith("attn_fwd_materialized"):
+        args += [_ptr(s), _ptr(p)]
+    with torch.cuda.device(q.device):
+        st = fn(*args, B, Hq, Hkv, N, d, ctypes.c_float(float(scale)),
+                _stream_handle(stream, q.device))
+    _raise(st, fn_name)
+
+
+def attn_fwd(q, k, v, o, lse, scale, stream=None):
+    """Fused tiled forward, bf16 I/O (C: attn_fwd)."""
+    _call("attn_fwd", torch.bfloat16, q, k, v, o, lse, None, None, scale, stream)
+
+
+def attn_fwd_f32(q, k, v, o, lse, scale, stream=None):
+    """Fused tiled forward, fp32 I/O (C: attn_fwd_f32)."""
+    _call("attn_fwd_f32", torch.float32, q, k, v, o, lse, None, None, scale, stream)
+
+
+def attn_fwd_materialized(q, k, v, o, lse, s, p, scale, stream=None):
+    """Three-kernel path that writes S (fp32) and P (bf16) (C: attn_fwd_materialized)."""
+    _call("attn_fwd_materialized", torch.bfloat16, q, k, v, o, lse, s, p, scale, stream)
+
+
+def attn_fwd_materialized_f32(q, k, v, o, lse, s, p, scale, stream=None):
+    """Three-kernel path, fp32 throughout (C: attn_fwd_materialized_f32)."""
+    _call("attn_fwd_materialized_f32", torch.float32, q, k, v, o, lse, s, p, scale, stream)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fwd(q, k, v, scale=None, stream=None):
+    """(o, lse) = attention forward; bf16 or fp32 by q's dtype; scale defaults to 1/sqrt(d)."""
+    B, Hq, _, N, d = _dims(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if q.dtype == torch.bfloat16:
+        attn_fwd(q, k, v, o, lse, _scale(scale, d), stream)
+    elif q.dtype == torch.float32:
+        attn_fwd_f32(q, k, v, o, lse, _scale(scale, d), stream)
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}; use bfloat16 or float32")
+    return o, lse
+
+
+def fwd_materialized(q, k, v, scale=None, stream=None):
+    """(o, lse, s, p) through the materialising three-kernel path."""
+    B, Hq, _, N, d = _dims(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    s = torch.empty((B, Hq, N, N), dtype=torch.float32, device=q.device)
+    p = torch.empty((B, Hq, N, N), dtype=q.dtype, device=q.device)
+    if q.dtype == torch.bfloat16:
+        attn_fwd_materialized(q, k, v, o, lse, s, p, _scale(scale, d), stream)
+    elif q.dtype == torch.float32:
+        attn_fwd_materialized_f32(q, k, v, o, lse, s, p, _scale(scale, d), stream)
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}; use bfloat16 or float32")
+    return o, lse, s, p

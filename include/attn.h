@@ -1,0 +1,126 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact scaled-dot-product attention forward
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (every entry point below computes it):
+ *
+ *   For each batch b in [0,B) and query head h in [0,Hq), with the shared
+ *   key/value head kv = h / (Hq / Hkv) (contiguous groups of query heads
+ *   share one K/V head: grouped-query attention, "efficient attention"
+ *   course chapter (deeplearning.wizardwu.top), class 3 and its methods
+ *   table), and each query row i:
+ *
+ *     S[i,j]     = scale * sum_c q[b,h,i,c] * k[b,kv,j,c]
+ *     O[b,h,i,:] = sum_j softmax_j(S[i,:]) * v[b,kv,j,:]
+ *     lse[b,h,i] = ln sum_j exp(S[i,j])
+ *
+ *   i.e. O = softmax(Q K^T * scale) V per head (aiknowledge.cn
+ *   "1.1 注意力计算的计算与显存瓶颈", section 1.1.1; blog
+ *   "attention 的显存线性化", section 一), with no mask and no dropout.
+ *   `scale` is usually 1/sqrt(d); any finite value is accepted.
+ *
+ * Layout: row-major, contiguous, head dimension fastest.
+ *   q, o : [B, Hq,  N, d]
+ *   k, v : [B, Hkv, N, d]
+ *   lse  : [B, Hq,  N]      float32, natural logarithm
+ *   s, p : [B, Hq,  N, N]   (materialising entry points only)
+ *
+ * Pointers: every array pointer is a DEVICE pointer, allocated and owned by
+ * the caller.  The library allocates no device memory and keeps no state
+ * between calls other than immutable device facts.  Outputs (o, lse, s, p)
+ * must not overlap the inputs or each other.
+ *
+ * Stream: `stream` is a hipStream_t passed as void*; NULL means the null
+ * stream.  Work is enqueued and the call returns without synchronising.
+ *
+ * Errors: every argument is checked before any HIP call; a failed check
+ * returns its attn_status_t code and enqueues nothing.  A launch failure
+ * reported by the HIP runtime returns ATTN_ERR_HIP.  No entry point prints,
+ * aborts or lets an exception escape.  attn_strerror() names a code.
+ *
+ * Sizes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128}.  Element
+ * offsets are computed in 64 bits; B*Hq*ceil(N/128) workgroups must fit the
+ * launch grid (< 2^31 / 256 workgroups).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,     /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,    /* B, Hq, Hkv or N < 1, or the problem is too large */
+  ATTN_ERR_GQA = 3,      /* Hq is not a multiple of Hkv */
+  ATTN_ERR_HEADDIM = 4,  /* d is not 64 or 128 */
+  ATTN_ERR_SCALE = 5,    /* scale is NaN or infinite */
+  ATTN_ERR_ALIGN = 6,    /* q/k/v/o/s/p not 16-byte aligned, or lse not 4-byte aligned */
+  ATTN_ERR_ALIAS = 7,    /* an output overlaps an input or another output */
+  ATTN_ERR_HIP = 8       /* the HIP runtime reported an error at launch */
+} attn_status_t;
+
+/*
+ * attn_fwd -- fused tiled forward, bfloat16 I/O, float32 accumulation.
+ *
+ * The IO-aware method: the query rows of each head are split into tiles and
+ * every tile streams all key/value tiles through on-chip memory, keeping a
+ * running row maximum m and exp-sum l and rescaling earlier partial sums by
+ * exp(m_old - m_new) when m grows (blog "attention 的显存线性化", section 三;
+ * "efficient attention" chapter, online-softmax paragraph).  S and P never
+ * reach device memory; O / l and lse are written once (aiknowledge.cn
+ * "3.1 性能模型：用 Roofline 与算术强度算清为什么快", section 3.1.3).
+ *
+ * q, k, v, o: bf16 (__bf16 / uint16 bit patterns).  lse: float32.
+ * Deterministic: the same inputs give bit-identical outputs.
+ */
+ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int N, int d, float scale, void* stream);
+
+/*
+ * attn_fwd_f32 -- the same fused tiled forward with float32 I/O and float32
+ * arithmetic throughout (no reduced-precision products).
+ */
+ATTN_API int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int Hq, int Hkv, int N, int d, float scale, void* stream);
+
+/*
+ * attn_fwd_materialized -- the "standard attention" the pages compare
+ * against (aiknowledge.cn "1.1 ...", sections 1.1.1 and 1.1.3): three
+ * kernels on `stream`, each a full device-memory round trip of an [N, N]
+ * matrix per head:
+ *   1. S = scale * Q K^T        written to s   (float32, [B,Hq,N,N])
+ *   2. P = row softmax of S     written to p   (bf16, [B,Hq,N,N]), and lse
+ *   3. O = P V                  written to o   (bf16)
+ * q, k, v, o, p: bf16.  s, lse: float32.  The caller sizes s and p
+ * (4 and 2 bytes per element) and may read them afterwards.
+ */
+ATTN_API int attn_fwd_materialized(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, float* s, void* p,
+                                   int B, int Hq, int Hkv, int N, int d, float scale,
+                                   void* stream);
+
+/*
+ * attn_fwd_materialized_f32 -- the materialising path with float32 I/O:
+ * q, k, v, o, s, p and lse all float32.
+ */
+ATTN_API int attn_fwd_materialized_f32(const float* q, const float* k, const float* v, float* o,
+                                       float* lse, float* s, float* p,
+                                       int B, int Hq, int Hkv, int N, int d, float scale,
+                                       void* stream);
+
+/* attn_strerror -- a static, NUL-terminated description of a status code. */
+ATTN_API const char* attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

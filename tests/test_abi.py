@@ -1,0 +1,113 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects
+bad arguments with the documented status before any HIP call (no GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+LIB = os.path.join(ROOT, "exact_io_aware_73_amd", "libattn.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"ATTN_API\s+[\w\s\*]+?\b(attn_\w+)\s*\(", text)
+
+
+def _status_codes():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(ATTN_\w+)\s*=\s*(\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} is not built (run __graft_entry__.build())")
+    l = ctypes.CDLL(LIB)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    l.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P]
+    l.attn_fwd_f32.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P]
+    l.attn_fwd_materialized.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, P]
+    l.attn_fwd_materialized_f32.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, P]
+    l.attn_strerror.argtypes = [I]
+    l.attn_strerror.restype = ctypes.c_char_p
+    return l
+
+
+def test_header_declares_the_entry_points():
+    assert set(_declared()) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_materialized",
+                                "attn_fwd_materialized_f32", "attn_strerror"}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_names_every_code(lib):
+    codes = _status_codes()
+    assert codes["ATTN_OK"] == 0
+    texts = {lib.attn_strerror(c).decode() for c in codes.values()}
+    assert len(texts) == len(codes)          # a distinct message per code
+    assert lib.attn_strerror(999) == b"unknown status"
+
+
+# Fake, never-dereferenced device addresses, far apart so nothing overlaps.
+# Every call below fails validation, which runs before any HIP call.
+A = 1 << 40
+Q, K, V, O, L, S, Pp = (A * (i + 1) for i in range(7))
+
+
+def _fwd(lib, fn, q=Q, k=K, v=V, o=O, lse=L, B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125):
+    return getattr(lib, fn)(q, k, v, o, lse, B, Hq, Hkv, N, d, ctypes.c_float(scale), None)
+
+
+def _mat(lib, fn, q=Q, k=K, v=V, o=O, lse=L, s=S, p=Pp, B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125):
+    return getattr(lib, fn)(q, k, v, o, lse, s, p, B, Hq, Hkv, N, d, ctypes.c_float(scale), None)
+
+
+FWD = ["attn_fwd", "attn_fwd_f32"]
+MAT = ["attn_fwd_materialized", "attn_fwd_materialized_f32"]
+
+
+@pytest.mark.parametrize("fn", FWD)
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), "ATTN_ERR_NULL"), (dict(k=None), "ATTN_ERR_NULL"), (dict(v=None), "ATTN_ERR_NULL"),
+    (dict(o=None), "ATTN_ERR_NULL"), (dict(lse=None), "ATTN_ERR_NULL"),
+    (dict(B=0), "ATTN_ERR_SHAPE"), (dict(Hq=0), "ATTN_ERR_SHAPE"), (dict(Hkv=0), "ATTN_ERR_SHAPE"),
+    (dict(N=0), "ATTN_ERR_SHAPE"), (dict(N=-5), "ATTN_ERR_SHAPE"),
+    (dict(Hq=3, Hkv=2), "ATTN_ERR_GQA"),
+    (dict(d=32), "ATTN_ERR_HEADDIM"), (dict(d=96), "ATTN_ERR_HEADDIM"), (dict(d=256), "ATTN_ERR_HEADDIM"),
+    (dict(scale=math.inf), "ATTN_ERR_SCALE"), (dict(scale=-math.inf), "ATTN_ERR_SCALE"),
+    (dict(scale=math.nan), "ATTN_ERR_SCALE"),
+    (dict(q=Q + 8), "ATTN_ERR_ALIGN"), (dict(k=K + 4), "ATTN_ERR_ALIGN"), (dict(v=V + 2), "ATTN_ERR_ALIGN"),
+    (dict(o=O + 8), "ATTN_ERR_ALIGN"), (dict(lse=L + 2), "ATTN_ERR_ALIGN"),
+    (dict(o=Q), "ATTN_ERR_ALIAS"), (dict(o=K + 16), "ATTN_ERR_ALIAS"), (dict(lse=V + 64), "ATTN_ERR_ALIAS"),
+    (dict(lse=O + 1024), "ATTN_ERR_ALIAS"),
+    (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, N=1 << 10), "ATTN_ERR_SHAPE"),
+])
+def test_fwd_rejects(lib, fn, kw, code):
+    assert _fwd(lib, fn, **kw) == _status_codes()[code]
+
+
+@pytest.mark.parametrize("fn", MAT)
+@pytest.mark.parametrize("kw,code", [
+    (dict(s=None), "ATTN_ERR_NULL"), (dict(p=None), "ATTN_ERR_NULL"), (dict(q=None), "ATTN_ERR_NULL"),
+    (dict(s=S + 4), "ATTN_ERR_ALIGN"), (dict(p=Pp + 8), "ATTN_ERR_ALIGN"),
+    (dict(s=Pp), "ATTN_ERR_ALIAS"), (dict(p=Q), "ATTN_ERR_ALIAS"), (dict(s=O), "ATTN_ERR_ALIAS"),
+    (dict(Hq=4, Hkv=3), "ATTN_ERR_GQA"), (dict(d=80), "ATTN_ERR_HEADDIM"),
+    (dict(scale=math.nan), "ATTN_ERR_SCALE"), (dict(N=0), "ATTN_ERR_SHAPE"),
+    (dict(B=64, Hq=64, Hkv=64, N=1 << 14), "ATTN_ERR_SHAPE"),   # softmax grid too large
+])
+def test_materialized_rejects(lib, fn, kw, code):
+    assert _mat(lib, fn, **kw) == _status_codes()[code]
+
+
+def test_python_binding_signatures_match_header():
+    """The binding's entry points carry the C names declared in the header."""
+    src = open(os.path.join(ROOT, "exact_io_aware_73_amd", "attn.py")).read()
+    for name in _declared():
+        assert re.search(rf"^def {name}\(", src, re.M), name

@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Run on an MI355X:  python -u -m pytest tests -m gpu -x -v
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import LSE_TOL, compare, half_ulp, round_to
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def attn():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from exact_io_aware_73_amd import attn as a   # fails loudly if libattn.so is missing
+    return a
+
+
+def _say(*msg):
+    print(*msg, file=sys.stderr, flush=True)
+
+
+def _dt(dtype):
+    return "bf16" if dtype == torch.bfloat16 else "f32"
+
+
+def _run(attn, q, k, v, scale):
+    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def _check_full(attn, q, k, v, scale, dtype, label):
+    _say(f"[parity] {label} q={tuple(q.shape)} k={tuple(k.shape)} {dtype} scale={scale}")
+    o, lse = _run(attn, q, k, v, scale)
+    O_ref, lse_ref = oracle.attention_ref(workloads.to_f64(q), workloads.to_f64(k),
+                                          workloads.to_f64(v), scale)
+    r = compare(workloads.to_f64(o), lse.numpy(), O_ref, lse_ref, _dt(dtype))
+    assert r["ok"], (label, r)
+    return r
+
+
+# ---------------------------------------------------------------------------
+# small and ragged shapes: every tile edge, the tail, GQA groupings
+SMALL_N = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 200, 1000]
+HEADS = [(1, 1, 1), (1, 4, 1), (2, 8, 2)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", SMALL_N)
+@pytest.mark.parametrize("B,Hq,Hkv", HEADS)
+def test_fused_bf16_small(attn, B, Hq, Hkv, N, d):
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=7 * N + d + Hq)
+    _check_full(attn, q, k, v, 1.0 / math.sqrt(d), torch.bfloat16, "fused bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 3, 31, 32, 33, 64, 65, 200, 1000])
+@pytest.mark.parametrize("B,Hq,Hkv", HEADS)
+def test_fused_f32_small(attn, B, Hq, Hkv, N, d):
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.float32, seed=11 * N + d + Hq)
+    _check_full(attn, q, k, v, 1.0 / math.sqrt(d), torch.float32, "fused f32")
+
+
+def test_single_head_fp32_workload(attn):
+    w = workloads.WORKLOADS["single_head_n256_d64_f32"]
+    q, k, v = workloads.make_inputs(w)
+    r = _check_full(attn, q, k, v, 1.0 / math.sqrt(w.d), torch.float32, w.name)
+    assert r["max_abs_O"] <= 1e-4 and r["max_abs_lse"] <= 1e-3
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5, 3.0])
+def test_fused_scales(attn, dtype, scale):
+    """Zero, negative and large scales (any finite scale is allowed)."""
+    q, k, v = workloads.random_inputs(1, 4, 2, 300, 128, dtype, seed=99)
+    _check_full(attn, q, k, v, scale, dtype, f"scale {scale}")
+
+
+def test_fused_wide_inputs(attn):
+    """Scores spread over hundreds: the running max moves often and far."""
+    q, k, v = workloads.random_inputs(1, 2, 1, 700, 64, torch.bfloat16, seed=5, std=6.0)
+    _check_full(attn, q, k, v, 1.0 / 8, torch.bfloat16, "wide scores")
+
+
+# ---------------------------------------------------------------------------
+# invariants through the GPU
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gpu_scale_zero_gives_mean(attn, dtype):
+    q, k, v = workloads.random_inputs(2, 4, 2, 333, 64, dtype, seed=3)
+    o, lse = _run(attn, q, k, v, 0.0)
+    mean = workloads.to_f64(v).mean(axis=2, keepdims=True).repeat(2, axis=1)
+    tol = 1e-2 if dtype == torch.bfloat16 else 1e-4
+    assert np.max(np.abs(workloads.to_f64(o) - mean)) <= tol + half_ulp(mean, _dt(dtype)).max()
+    assert np.max(np.abs(lse.numpy() - math.log(333))) <= LSE_TOL
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gpu_single_key(attn, dtype):
+    """N = 1: O = V_0 exactly (one weight of exactly 1), lse = scale q.k_0."""
+    q, k, v = workloads.random_inputs(3, 4, 4, 1, 128, dtype, seed=4)
+    o, lse = _run(attn, q, k, v, 0.3)
+    assert torch.equal(o, v)
+    ref = 0.3 * np.einsum("bhnd,bhnd->bhn", workloads.to_f64(q), workloads.to_f64(k))
+    assert np.max(np.abs(lse.numpy() - ref)) <= LSE_TOL
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gpu_constant_v(attn, dtype):
+    q, k, _ = workloads.random_inputs(1, 2, 1, 517, 128, dtype, seed=6)
+    row = torch.randn(1, 1, 1, 128, generator=torch.Generator().manual_seed(1)).to(dtype)
+    v = row.expand(1, 1, 517, 128).contiguous()
+    o, _ = _run(attn, q, k, v, 1 / math.sqrt(128))
+    ref = workloads.to_f64(row).repeat(2, axis=1)
+    tol = 1e-2 if dtype == torch.bfloat16 else 1e-4
+    assert np.max(np.abs(workloads.to_f64(o) - ref)) <= tol
+
+
+def test_gpu_one_hot(attn):
+    """A key far ahead of all others selects its V row."""
+    N, d = 256, 64
+    q = torch.zeros(1, 1, N, d)
+    k = torch.rand(1, 1, N, d, generator=torch.Generator().manual_seed(2)) - 0.5
+    for c in range(d):
+        k[0, 0, 3 * c] = 0.0
+        k[0, 0, 3 * c, c] = 8.0
+    for i in range(N):
+        q[0, 0, i, i % d] = 8.0
+    v = torch.randn(1, 1, N, d, generator=torch.Generator().manual_seed(3))
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    o, _ = _run(attn, q, k, v, 1.0)   # winner 64, others <= 4
+    for i in range(N):
+        assert torch.equal(o[0, 0, i], v[0, 0, 3 * (i % d)])
+
+
+def test_gpu_gqa_equals_repeated_heads(attn):
+    """GQA equals MHA on repeated K/V heads, bit for bit."""
+    q, k, v = workloads.random_inputs(2, 8, 2, 777, 128, torch.bfloat16, seed=8)
+    o1, l1 = _run(attn, q, k, v, 0.1)
+    o2, l2 = _run(attn, q, k.repeat_interleave(4, dim=1).contiguous(),
+                  v.repeat_interleave(4, dim=1).contiguous(), 0.1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gpu_shift_keys(attn):
+    """K' = K + u: compare against the oracle on the same (re-rounded) K'."""
+    q, k, v = workloads.random_inputs(1, 2, 2, 400, 128, torch.bfloat16, seed=10)
+    u = torch.randn(128, generator=torch.Generator().manual_seed(11)) * 2
+    k2 = (k.float() + u).bfloat16().contiguous()
+    _check_full(attn, q, k2, v, 1 / math.sqrt(128), torch.bfloat16, "shifted K")
+
+
+def test_gpu_deterministic_and_stream(attn):
+    q, k, v = workloads.random_inputs(2, 8, 2, 1500, 128, torch.bfloat16, seed=12)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = attn.fwd(q, k, v)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = attn.fwd(q, k, v, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_python_rejects_bad_arguments(attn):
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        attn.fwd(q, k[:, :, :4].contiguous(), k)
+    with pytest.raises(ValueError):
+        attn.fwd(q, k, k, scale=float("nan"))
+    with pytest.raises(ValueError):
+        attn.fwd(torch.zeros(1, 2, 8, 96, dtype=torch.bfloat16, device="cuda"),
+                 torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device="cuda"),
+                 torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        attn.fwd(q.half(), k.half(), k.half())
+
+
+# ---------------------------------------------------------------------------
+# materialising path: O, lse, and the S and P it writes
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 1, 1, 1, 64), (1, 2, 1, 37, 64), (2, 4, 2, 129, 128),
+                                           (1, 2, 2, 256, 64), (1, 4, 1, 300, 128), (1, 1, 1, 1000, 64)])
+def test_materialized_small(attn, dtype, B, Hq, Hkv, N, d):
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, dtype, seed=13 * N + d)
+    scale = 1 / math.sqrt(d)
+    _say(f"[parity] materialized {dtype} {(B, Hq, Hkv, N, d)}")
+    o, lse, s, p = attn.fwd_materialized(q.cuda(), k.cuda(), v.cuda(), scale)
+    torch.cuda.synchronize()
+    O_ref, lse_ref, S_ref, P_ref = oracle.attention_ref_sp(
+        workloads.to_f64(q), workloads.to_f64(k), workloads.to_f64(v), scale)
+    r = compare(workloads.to_f64(o), lse.cpu().numpy(), O_ref, lse_ref, _dt(dtype))
+    assert r["ok"], r
+    s64 = s.cpu().double().numpy()
+    p64 = workloads.to_f64(p)
+    # S: fp32 accumulation of exact products; P: the I/O format's rounding
+    assert np.max(np.abs(s64 - S_ref)) <= 1e-4
+    assert np.max(np.abs(p64 - P_ref) - 2 * half_ulp(P_ref, _dt(dtype))) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size, in the launch configuration bench.py
+# times: sampled rows against the oracle, properties on every row, and
+# bitwise determinism
+FULL = ["gpt2_medium_b64_h16_n1024_d64", "long_b4_h32_n4096_d128", "gqa_b2_hq32_hkv8_n8192_d128",
+        "gqa_b2_hq32_hkv8_n8192_d128_kscaled", "long_context_b1_h8_n32768_d128"]
+
+
+def sample_rows(N, rng, n_rand=32):
+    rows = set(range(min(16, N))) | set(range(max(0, N - 16), N))
+    rows |= set(rng.choice(N, size=min(n_rand, N), replace=False).tolist())
+    return sorted(rows)
+
+
+def check_sampled(q, k, v, o, lse, scale, dtype, seed=0):
+    """Oracle on sampled rows of three heads (first, last, one random)."""
+    B, Hq, N, d = q.shape
+    rng = np.random.default_rng(seed)
+    heads = {(0, 0), (B - 1, Hq - 1), (int(rng.integers(B)), int(rng.integers(Hq)))}
+    worst = None
+    for (b, h) in sorted(heads):
+        kv = oracle.kv_head(h, Hq, k.shape[1])
+        rows = sample_rows(N, rng)
+        O_ref, l_ref = oracle.attention_head(workloads.to_f64(q[b, h]), workloads.to_f64(k[b, kv]),
+                                             workloads.to_f64(v[b, kv]), scale, rows=rows)
+        r = compare(workloads.to_f64(o[b, h, rows]), lse[b, h, rows].numpy(), O_ref, l_ref, dtype)
+        assert r["ok"], ((b, h), r)
+        if worst is None or r["max_abs_O"] > worst["max_abs_O"]:
+            worst = r
+    return worst
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload(attn, name):
+    w = workloads.WORKLOADS[name]
+    _say(f"[parity] full workload {name}")
+    q, k, v = workloads.make_inputs(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    scale = 1 / math.sqrt(w.d)
+    o1, l1 = attn.fwd(qd, kd, vd, scale)
+    o2, l2 = attn.fwd(qd, kd, vd, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "not deterministic"
+    # every row: finite, a convex combination of V rows, lse >= the row max
+    assert torch.isfinite(o1).all() and torch.isfinite(l1).all()
+    vmax = vd.float().abs().amax(dim=(2, 3))                         # [B, Hkv]
+    vmax = vmax.repeat_interleave(w.Hq // w.Hkv, dim=1)[:, :, None, None]
+    assert (o1.float().abs() <= vmax * (1 + 2 ** -6) + 1e-6).all()
+    o, lse = o1.cpu(), l1.cpu()
+    del o1, o2, l1, l2
+    r = check_sampled(q, k, v, o, lse, scale, w.dtype, seed=w.seed)
+    _say(f"[parity] {name}: {r}")
+
+
+def test_materialized_long_workload(attn):
+    """The long-sequence workload through the materialising path (S is 8.6 GB)."""
+    w = workloads.WORKLOADS["long_b4_h32_n4096_d128"]
+    _say("[parity] materialized full long workload")
+    q, k, v = workloads.make_inputs(w)
+    scale = 1 / math.sqrt(w.d)
+    o, lse, s, p = attn.fwd_materialized(q.cuda(), k.cuda(), v.cuda(), scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = sample_rows(w.N, rng, 8)
+    for (b, h) in [(0, 0), (w.B - 1, w.Hq - 1)]:
+        qh, kh, vh = (workloads.to_f64(t[b, h]) for t in (q, k, v))
+        S_ref = oracle.head_scores(qh[rows], kh, scale)
+        P_ref, l_ref = oracle.softmax_rows(S_ref)
+        O_ref = P_ref @ vh
+        assert np.max(np.abs(s[b, h, rows].cpu().double().numpy() - S_ref)) <= 1e-4
+        p64 = workloads.to_f64(p[b, h, rows])
+        assert np.max(np.abs(p64 - P_ref) - 2 * half_ulp(P_ref, "bf16")) <= 1e-5
+        r = compare(workloads.to_f64(o[b, h, rows]), lse[b, h, rows].cpu().numpy(), O_ref, l_ref, "bf16")
+        assert r["ok"], r
+    del s, p
