@@ -1,0 +1,85 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+    python -m exact_io_aware_73_amd.profiling stats  <trace_kernel_stats.csv> <out.txt> "<command>"
+    python -m exact_io_aware_73_amd.profiling counters <workload> <fetch.csv> <write.csv>
+        <copy_fetch.csv> <copy_write.csv> <copy_mib> <out.json> "<commands>"
+
+``stats`` turns a ``--kernel-trace --stats`` CSV into a short text table.
+``counters`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
+the fused kernel, and the same two counters read on a plain device copy of
+known size, into HBM bytes per launch: each counter (KiB per dispatch) is
+scaled by known copy bytes / the counter's reading on the copy.
+"""
+from __future__ import annotations
+
+import csv
+import json
+import statistics
+import sys
+
+FUSED_KERNEL = "attn_fwd_bf16_kernel"
+COPY_KERNEL = "copyBuffer"
+
+
+def kernel_stats_table(path: str, command: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    lines = [f"command: {command}", "",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in rows:
+        name = r["Name"]
+        short = name if len(name) <= 60 else name[:57] + "..."
+        lines.append(f"{short:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                     f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} "
+                     f"{float(r['Percentage']):6.2f}")
+    lines.append("")
+    lines.append("full kernel names:")
+    lines += [f"  {r['Name']}" for r in rows]
+    return "\n".join(lines) + "\n"
+
+
+def counter_kib(path: str, kernel_substr: str):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise ValueError(f"no dispatch of a kernel matching {kernel_substr!r} in {path}")
+    return vals
+
+
+def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib,
+                     commands, kernel_source_sha):
+    copy_bytes = int(copy_mib) << 20
+    cf = statistics.median(counter_kib(copy_fetch_csv, COPY_KERNEL))
+    cw = statistics.median(counter_kib(copy_write_csv, COPY_KERNEL))
+    f_scale = copy_bytes / (cf * 1024)
+    w_scale = copy_bytes / (cw * 1024)
+    fk = counter_kib(fetch_csv, FUSED_KERNEL)
+    wk = counter_kib(write_csv, FUSED_KERNEL)
+    fetch = statistics.median(fk) * 1024 * f_scale
+    write = statistics.median(wk) * 1024 * w_scale
+    return {
+        "workload": workload, "kernel": FUSED_KERNEL,
+        "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+        "copy_probe_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+        "hbm_read_bytes_per_launch": round(fetch), "hbm_write_bytes_per_launch": round(write),
+        "hbm_bytes_per_launch": round(fetch + write),
+        "kernel_source_sha": kernel_source_sha, "commands": commands,
+    }
+
+
+def main(argv):
+    if argv[0] == "stats":
+        _, src, out, cmd = argv
+        open(out, "w").write(kernel_stats_table(src, cmd))
+    elif argv[0] == "counters":
+        _, wl, f, w, cf, cw, mib, out, cmds, sha = argv
+        rec = counters_summary(wl, f, w, cf, cw, int(mib), cmds, sha)
+        json.dump(rec, open(out, "w"), indent=1)
+        print(json.dumps({k: rec[k] for k in ("workload", "hbm_read_bytes_per_launch",
+                                               "hbm_write_bytes_per_launch")}))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
