@@ -11,16 +11,19 @@
 //    block with v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the
 //    wave's Q rows resident in VGPRs as the B operand).  In that output
 //    layout a lane owns ONE query (column l % 32) and 16 of the 32 keys, so
-//    the row max / row sum are in-lane reductions plus one exchange with
-//    lane l ^ 32.
+//    the row max / row sum are in-lane reductions plus one v_permlane32_swap
+//    with the other half-wave.
 //  * O^T = V^T P^T on the same MFMA: P^T comes straight from the S^T
-//    accumulator registers (rounded to bf16), V^T from LDS, and the O^T
-//    accumulator again gives each lane one query, so the rescale by
-//    exp(m_old - m_new) is a per-lane scalar.
-//  * K tiles are staged row-major, V tiles transposed (V^T, keys fastest),
-//    both padded so the MFMA-operand reads and the staging writes are free
-//    of LDS bank conflicts; two stages, the next tile's global loads in
-//    flight while the current tile is computed.
+//    accumulator registers (rounded to bf16); the V^T operand is read from
+//    the row-major V tile with ds_read_b64_tr_b16, which hands each lane
+//    four consecutive keys of one d column.  The O^T accumulator again gives
+//    each lane one query, so the rescale by exp(m_old - m_new) is a per-lane
+//    scalar.
+//  * K and V tiles go global -> LDS directly (global_load_lds_dwordx4, no
+//    staging registers), two stages, the next tile in flight while the
+//    current one is computed.  Rows sit unpadded with their 16-byte chunks
+//    XOR-swizzled by the row index, so both the MFMA operand reads of K and
+//    the transposing reads of V are free of LDS bank conflicts.
 //  * The scale is folded into exp2: p = 2^(s * scale * log2 e - m).  The
 //    running max is only moved when some row's max grows by more than
 //    kRescaleLog2 (softmax is unchanged by any common shift of a row, the
@@ -31,22 +34,82 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "bf16_tiles.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace attn {
 namespace {
 
-constexpr float kRescaleLog2 = 8.0f;   // move m only when it grows by > 2^8
+constexpr int kFWaves = 4;
+constexpr int kFThreads = kFWaves * kWave;
+constexpr int kFRows = 32;                   // query rows per wave
+constexpr int kFBr = kFWaves * kFRows;       // query rows per workgroup
+constexpr float kRescaleLog2 = 8.0f;         // move m only when it grows by > 2^8
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+struct FGeo {
+  static constexpr int kBc = (D == 128) ? 64 : 128;    // keys per tile
+  static constexpr int kKB = kBc / 32;                 // 32-key blocks per tile
+  static constexpr int kKSteps = D / 16;               // MFMA k-steps over d
+  static constexpr int kDB = D / 32;                   // 32-wide d blocks
+  static constexpr int kCPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int kTile = kBc * D;                // bf16 elements of K (or V)
+  static constexpr int kStage = 2 * kTile;             // K then V
+  static constexpr int kDmaPerWave = kTile / 8 / kWave / kFWaves;   // 16-B loads per lane per tile
+  static_assert(kDmaPerWave * 8 * kWave * kFWaves == kTile, "tile must split over the waves");
+};
+
+// Chunk swizzle: chunk c of row r is stored at chunk c ^ swz(r).  swz maps
+// rows r..r+7 (r % 8 == 0) onto all of 0..7, and rows r..r+3 (r % 4 == 0)
+// onto {2k + b}, which is what the two read patterns need.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Issue the direct loads of one K or V tile (keys j0 .. j0 + kBc - 1).
+// Rows past N are clamped to row N - 1: finite data that the softmax masks.
+template <int D>
+__device__ __forceinline__ void dma_tile(const __bf16* __restrict__ head, int j0, int N,
+                                         __bf16* lds_tile, int wave, int lane) {
+  using G = FGeo<D>;
+#pragma unroll
+  for (int i = 0; i < G::kDmaPerWave; ++i) {
+    const int slot = (wave * G::kDmaPerWave + i) * kWave;   // first chunk of this instruction
+    const int g = slot + lane;
+    const int row = g / G::kCPR;
+    const int c = (g % G::kCPR) ^ swz(row);                 // logical chunk stored here
+    const int key = min(j0 + row, N - 1);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(head + (int64_t)key * D + c * 8),
+                                     (lds_void*)(lds_tile + slot * 8), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Across the two half-waves (lane l and l ^ 32): both get the combined value.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_min(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D, bool kNegScale>
-__global__ __launch_bounds__(kThreads, 2)
+__global__ __launch_bounds__(kFThreads, 2)
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                           const __bf16* __restrict__ v, __bf16* __restrict__ o,
                           float* __restrict__ lse, int Hq, int Hkv, int N, float c_log2,
                           int n_qtiles, uint32_t n_xcd) {
-  using G = Geo<D>;
+  using G = FGeo<D>;
   __shared__ __align__(16) __bf16 smem[2 * G::kStage];
 
   const int tid = threadIdx.x;
@@ -71,7 +134,12 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   const __bf16* kh = k + head_kv * D;
   const __bf16* vh = v + head_kv * D;
 
-  const int qrow = qt * kBr + wave * kRowsPerWave + l32;   // this lane's query
+  const int n_tiles = (N + G::kBc - 1) / G::kBc;
+  // first tile in flight before anything else
+  dma_tile<D>(kh, 0, N, smem, wave, lane);
+  dma_tile<D>(vh, 0, N, smem + G::kTile, wave, lane);
+
+  const int qrow = qt * kFBr + wave * kFRows + l32;   // this lane's query
   const bool qvalid = qrow < N;
 
   // ---- Q^T fragments: lane holds d = 16 s + 8 hh .. +7 of its query -------
@@ -85,36 +153,53 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     }
   }
 
+  // ---- per-lane LDS offsets (elements) -------------------------------------
+  // K operand: row kb*32 + l32, chunk 2 s + hh, swizzled by the row.
+  int koff[G::kKSteps];
+#pragma unroll
+  for (int s = 0; s < G::kKSteps; ++s) koff[s] = l32 * D + (((2 * s + hh) ^ swz(l32)) * 8);
+  // V^T operand (transposing read): in each 16-lane group, lane i points at
+  // key (i / 4) of a 4-key run and d columns 4 (i % 4) .. +3 of the group's
+  // 16 columns; it receives key run 0..3 of column (group base + i).
+  const int li = lane & 15;
+  const int dhalf = (lane >> 4) & 1;
+  const int vrow = 4 * hh + (li >> 2);          // row within a 16-key step (plus 8 for slots 4..7)
+  int voff[G::kDB];
+#pragma unroll
+  for (int db = 0; db < G::kDB; ++db) {
+    const int dcol = db * 32 + dhalf * 16 + 4 * (li & 3);
+    voff[db] = vrow * D + (((dcol >> 3) ^ swz(vrow)) * 8) + (dcol & 7);
+  }
+
   f32x16 oacc[G::kDB];
 #pragma unroll
   for (int i = 0; i < G::kDB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY;   // running max of the log2-scaled scores
   float l_run = 0.0f;        // this lane's part of the exp-sum (its 16 keys per block)
 
-  const int n_tiles = (N + G::kBc - 1) / G::kBc;
-  Regs regs;
-  load_tile<D>(regs, kh, vh, 0, N, tid);
-  store_tile<D>(regs, smem, smem + G::kKElems, tid);
+  wait_dma();
   __syncthreads();
 
   for (int jt = 0; jt < n_tiles; ++jt) {
-    const bool has_next = jt + 1 < n_tiles;
-    if (has_next) load_tile<D>(regs, kh, vh, (jt + 1) * G::kBc, N, tid);
-
     const __bf16* ks = smem + (jt & 1) * G::kStage;
-    const __bf16* vts = ks + G::kKElems;
+    const __bf16* vs = ks + G::kTile;
+    if (jt + 1 < n_tiles) {
+      __bf16* nxt = smem + ((jt + 1) & 1) * G::kStage;
+      dma_tile<D>(kh, (jt + 1) * G::kBc, N, nxt, wave, lane);
+      dma_tile<D>(vh, (jt + 1) * G::kBc, N, nxt + G::kTile, wave, lane);
+    }
 
     // ---- S^T = K Q^T for kKB blocks of 32 keys ---------------------------
     f32x16 sacc[G::kKB];
 #pragma unroll
     for (int kb = 0; kb < G::kKB; ++kb) {
-      sacc[kb] = f32x16{};
-      const __bf16* kr = ks + (kb * 32 + l32) * G::kKStr + 8 * hh;
+      bf16x8 kf[G::kKSteps];
 #pragma unroll
-      for (int s = 0; s < G::kKSteps; ++s) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * s));
-        sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
-      }
+      for (int s = 0; s < G::kKSteps; ++s)
+        kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + kb * 32 * D + koff[s]));
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < G::kKSteps; ++s) sacc[kb] = mfma32x32x16(kf[s], qf[s], sacc[kb]);
     }
 
     // ---- online softmax on this lane's 16 * kKB scores -------------------
@@ -122,30 +207,36 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     const bool tail = j0 + G::kBc > N;
     float ext;
     if (!tail) {
-      ext = kNegScale ? INFINITY : -INFINITY;
+      // tree of max (min) over the lane's scores
+      float t[G::kKB * 4];
 #pragma unroll
       for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          ext = kNegScale ? fminf(ext, sacc[kb][e]) : fmaxf(ext, sacc[kb][e]);
-      ext = kNegScale ? fminf(ext, __shfl_xor(ext, 32)) : fmaxf(ext, __shfl_xor(ext, 32));
-      ext *= c_log2;   // max over the row of s * c_log2
+        for (int r = 0; r < 4; ++r) {
+          const f32x16& a = sacc[kb];
+          t[kb * 4 + r] = kNegScale
+              ? fminf(fminf(a[4 * r], a[4 * r + 1]), fminf(a[4 * r + 2], a[4 * r + 3]))
+              : fmaxf(fmaxf(a[4 * r], a[4 * r + 1]), fmaxf(a[4 * r + 2], a[4 * r + 3]));
+        }
+#pragma unroll
+      for (int w = G::kKB * 4; w > 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w / 2; ++i)
+          t[i] = kNegScale ? fminf(t[i], t[i + w / 2]) : fmaxf(t[i], t[i + w / 2]);
+      ext = kNegScale ? xhalf_min(t[0]) : xhalf_max(t[0]);
     } else {
-      // scale first, then mask keys >= N with -inf
+      // keys >= N hold clamped copies of row N - 1: leave them out
+      float e2 = kNegScale ? INFINITY : -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          sacc[kb][e] = key < N ? sacc[kb][e] * c_log2 : -INFINITY;
+          if (key < N) e2 = kNegScale ? fminf(e2, sacc[kb][e]) : fmaxf(e2, sacc[kb][e]);
         }
-      ext = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ext = fmaxf(ext, sacc[kb][e]);
-      ext = fmaxf(ext, __shfl_xor(ext, 32));
+      ext = kNegScale ? xhalf_min(e2) : xhalf_max(e2);
     }
+    ext *= c_log2;   // the row's max of s * c_log2
 
     // move the running max only when some row's max grows by > 2^kRescaleLog2
     if (__any(ext > m_run + kRescaleLog2)) {
@@ -157,52 +248,59 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
       for (int i = 0; i < G::kDB; ++i) oacc[i] *= alpha;
     }
 
-    bf16x8 pf[G::kKB][2];
-    float lsum = 0.0f;
+    float p[G::kKB][16];
 #pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb) {
-      float p[16];
+    for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = tail ? exp2_fast(sacc[kb][e] - m_run)
-                    : exp2_fast(__builtin_fmaf(sacc[kb][e], c_log2, -m_run));
-        lsum += p[e];
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 u;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) u[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
-        pf[kb][s2] = as_bf16x8(u);
-      }
-    }
-    l_run += lsum;
-
-    // ---- O^T += V^T P^T ---------------------------------------------------
-    // P^T slot (hh, e) of k-step s2 in block kb holds key kb*32 + 16 s2 +
-    // 8 (e / 4) + 4 hh + e % 4; the V^T operand reads the same keys.
-#pragma unroll
-    for (int db = 0; db < G::kDB; ++db) {
-      const __bf16* vr = vts + (db * 32 + l32) * G::kVStr + 4 * hh;
+      for (int e = 0; e < 16; ++e) p[kb][e] = exp2_fast(__builtin_fmaf(sacc[kb][e], c_log2, -m_run));
+    if (tail) {
 #pragma unroll
       for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int off = kb * 32 + 16 * s2;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + off);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + off + 8);
-          const u32x4 u = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = mfma32x32x16(as_bf16x8(u), pf[kb][s2], oacc[db]);
+        for (int e = 0; e < 16; ++e) {
+          const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          if (key >= N) p[kb][e] = 0.0f;
         }
     }
+    {
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ps[e & 3] += p[kb][e];
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
 
-    if (has_next) store_tile<D>(regs, smem + ((jt + 1) & 1) * G::kStage,
-                                smem + ((jt + 1) & 1) * G::kStage + G::kKElems, tid);
+    // ---- O^T += V^T P^T ---------------------------------------------------
+    // P^T slot (hh, e) of k-step s2 in block kb holds key
+    // kb*32 + 16 s2 + 8 (e / 4) + 4 hh + e % 4; the transposing V reads
+    // fetch the same keys: slots 0..3 from rows +0..3, slots 4..7 from +8..11.
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 pu;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pu[w] = pack_bf16x2(p[kb][8 * s2 + 2 * w], p[kb][8 * s2 + 2 * w + 1]);
+        const bf16x8 pf = as_bf16x8(pu);
+        const int rbase = (kb * 32 + 16 * s2) * D;
+#pragma unroll
+        for (int db = 0; db < G::kDB; ++db) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vs + rbase + voff[db]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vs + rbase + 8 * D + voff[db]));
+          const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, a8), pf, oacc[db]);
+        }
+      }
+
+    wait_dma();
     __syncthreads();
   }
 
   // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2 ------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xhalf_sum(l_run);
   if (qvalid) {
     const float inv = 1.0f / l_tot;
     __bf16* orow = o + (head_q + qrow) * D;
@@ -221,21 +319,20 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
 
 template <int D, bool kNeg>
 hipError_t launch_d(const FwdArgs& a) {
-  const int n_qtiles = (a.N + kBr - 1) / kBr;
+  const int n_qtiles = (a.N + kFBr - 1) / kFBr;
   const uint64_t grid = (uint64_t)n_qtiles * a.Hq * a.B;
   const float c_log2 = a.scale * 1.44269504088896341f;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, kNeg>), dim3((uint32_t)grid), dim3(kThreads),
-                     0, a.stream, static_cast<const __bf16*>(a.q),
-                     static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                     static_cast<__bf16*>(a.o), a.lse, a.Hq, a.Hkv, a.N, c_log2, n_qtiles,
-                     (uint32_t)a.n_xcd);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, kNeg>), dim3((uint32_t)grid), dim3(kFThreads), 0,
+                     a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.Hq,
+                     a.Hkv, a.N, c_log2, n_qtiles, (uint32_t)a.n_xcd);
   return hipGetLastError();
 }
 
 }  // namespace
 
 uint64_t fwd_bf16_grid(int B, int Hq, int N) {
-  return (uint64_t)((N + kBr - 1) / kBr) * Hq * B;
+  return (uint64_t)((N + kFBr - 1) / kFBr) * Hq * B;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
