@@ -29,6 +29,14 @@ CFLAGS = [
 ]
 
 
+# Extra flags per source file.  The fused bf16 kernel keeps its MFMA
+# accumulators in architectural VGPRs, next to the softmax that reads them,
+# instead of moving every score through the accumulation registers.
+FILE_FLAGS = {
+    "attn_fwd_bf16_rows64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line
@@ -47,7 +55,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        out = _run([HIPCC, *CFLAGS, "-c", src, "-o", obj])
+        extra = FILE_FLAGS.get(os.path.basename(src), [])
+        out = _run([HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj])
         if verbose and out.strip():
             print(out, file=sys.stderr)
         return obj

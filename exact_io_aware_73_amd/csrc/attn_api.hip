@@ -92,13 +92,18 @@ int fwd_impl(bool bf16, const void* q, const void* k, const void* v, void* o, fl
              int Hq, int Hkv, int N, int d, float scale, void* stream) {
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
   if (st != ATTN_OK) return st;
-  const uint64_t grid = bf16 ? attn::fwd_bf16_grid(B, Hq, N) : attn::fwd_f32_grid(B, Hq, N);
+  const bool rows64 = attn::fwd_bf16_use_rows64(d);
+  const uint64_t grid = !bf16 ? attn::fwd_f32_grid(B, Hq, N)
+                      : rows64 ? attn::fwd_bf16_rows64_grid(B, Hq, N)
+                               : attn::fwd_bf16_rows32_grid(B, Hq, N);
   if (grid > kMaxWorkgroups) return ATTN_ERR_SHAPE;
   const int elem = bf16 ? 2 : 4;
   st = check_alias(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, elem, 0);
   if (st != ATTN_OK) return st;
   const attn::FwdArgs a = make_args(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, scale, stream);
-  return to_status(bf16 ? attn::launch_fwd_bf16(a) : attn::launch_fwd_f32(a));
+  return to_status(!bf16 ? attn::launch_fwd_f32(a)
+                   : rows64 ? attn::launch_fwd_bf16_rows64(a)
+                            : attn::launch_fwd_bf16_rows32(a));
 }
 
 int materialized_impl(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse,

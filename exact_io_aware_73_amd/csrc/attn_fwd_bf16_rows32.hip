@@ -1,4 +1,5 @@
-// attn_fwd_bf16.hip -- fused, tiled attention forward for gfx950, bf16 I/O.
+// attn_fwd_bf16_rows32.hip -- fused, tiled attention forward for gfx950,
+// bf16 I/O, one 32-row query block per wave (used for head dim 64).
 //
 // The IO-aware forward (blog "attention 的显存线性化", section 三; the
 // "efficient attention" chapter's online-softmax paragraph): one workgroup
@@ -69,34 +70,45 @@ struct FGeo {
 // onto {2k + b}, which is what the two read patterns need.
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
-// Issue the direct loads of one K or V tile (keys j0 .. j0 + kBc - 1).
-// Rows past N are clamped to row N - 1: finite data that the softmax masks.
+// Issue the direct loads of one K or V tile (keys j0 .. j0 + kBc - 1) into
+// the LDS tile at byte address lds_tile.  The buffer covers only rows
+// j0 .. N-1: rows past N read as zeros (the softmax masks them) and nothing
+// is read out of bounds.  Issued as inline assembly so the compiler does not
+// see an LDS write in flight and does not hold the reads of the other buffer
+// behind it; wait_dma() and the barrier order these loads against readers.
 template <int D>
 __device__ __forceinline__ void dma_tile(const __bf16* __restrict__ head, int j0, int N,
-                                         __bf16* lds_tile, int wave, int lane) {
+                                         uint32_t lds_tile, int wave, const int* dvoff) {
   using G = FGeo<D>;
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(N - j0, G::kBc)));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(head) + (int64_t)min(j0, N) * D, (short)0, rows * D * 2, 0x00020000);
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
-    const int slot = (wave * G::kDmaPerWave + i) * kWave;   // first chunk of this instruction
-    const int g = slot + lane;
-    const int row = g / G::kCPR;
-    const int c = (g % G::kCPR) ^ swz(row);                 // logical chunk stored here
-    const int key = min(j0 + row, N - 1);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(head + (int64_t)key * D + c * 8),
-                                     (lds_void*)(lds_tile + slot * 8), 16, 0, 0);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        lds_tile + (uint32_t)((wave * G::kDmaPerWave + i) * kWave * 16));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 ::"s"(dst), "v"(dvoff[i]), "s"(rs) : "memory");
   }
 }
 
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) as a real instruction (expcnt and lgkmcnt left at
+// their maxima), so the compiler knows every vector load has completed.
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// IEEE-754 maximum / minimum (v_maximum3_f32 / v_minimum3_f32 on gfx950):
+// unlike fmaxf they need no canonicalisation of MFMA results first.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 
 // Across the two half-waves (lane l and l ^ 32): both get the combined value.
 __device__ __forceinline__ float xhalf_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xhalf_min(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmin(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -105,18 +117,32 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 template <int D, bool kNegScale>
 __global__ __launch_bounds__(kFThreads, 2)
-void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                           const __bf16* __restrict__ v, __bf16* __restrict__ o,
                           float* __restrict__ lse, int Hq, int Hkv, int N, float c_log2,
                           int n_qtiles, uint32_t n_xcd) {
   using G = FGeo<D>;
   __shared__ __align__(16) __bf16 smem[2 * G::kStage];
 
+  const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) __bf16*)smem);
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+
+  // direct loads: instruction i of this wave fills 16-byte chunks
+  // slot .. slot + 63 of a tile; lane's chunk g = slot + lane holds logical
+  // chunk (g % kCPR) ^ swz(row) of row g / kCPR
+  int dvoff[G::kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < G::kDmaPerWave; ++i) {
+    const int g = (wave * G::kDmaPerWave + i) * kWave + lane;
+    const int row = g / G::kCPR;
+    const int c = (g % G::kCPR) ^ swz(row);
+    dvoff[i] = (row * D + c * 8) * 2;
+  }
 
   // ---- which (b, head, query tile) this workgroup owns -------------------
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
@@ -136,8 +162,8 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
 
   const int n_tiles = (N + G::kBc - 1) / G::kBc;
   // first tile in flight before anything else
-  dma_tile<D>(kh, 0, N, smem, wave, lane);
-  dma_tile<D>(vh, 0, N, smem + G::kTile, wave, lane);
+  dma_tile<D>(kh, 0, N, lds, wave, dvoff);
+  dma_tile<D>(vh, 0, N, lds + G::kTile * 2, wave, dvoff);
 
   const int qrow = qt * kFBr + wave * kFRows + l32;   // this lane's query
   const bool qvalid = qrow < N;
@@ -184,9 +210,9 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     const __bf16* ks = smem + (jt & 1) * G::kStage;
     const __bf16* vs = ks + G::kTile;
     if (jt + 1 < n_tiles) {
-      __bf16* nxt = smem + ((jt + 1) & 1) * G::kStage;
-      dma_tile<D>(kh, (jt + 1) * G::kBc, N, nxt, wave, lane);
-      dma_tile<D>(vh, (jt + 1) * G::kBc, N, nxt + G::kTile, wave, lane);
+      const uint32_t nxt = lds + ((jt + 1) & 1) * G::kStage * 2;
+      dma_tile<D>(kh, (jt + 1) * G::kBc, N, nxt, wave, dvoff);
+      dma_tile<D>(vh, (jt + 1) * G::kBc, N, nxt + G::kTile * 2, wave, dvoff);
     }
 
     // ---- S^T = K Q^T for kKB blocks of 32 keys ---------------------------
@@ -215,24 +241,24 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         for (int r = 0; r < 4; ++r) {
           const f32x16& a = sacc[kb];
           t[kb * 4 + r] = kNegScale
-              ? fminf(fminf(a[4 * r], a[4 * r + 1]), fminf(a[4 * r + 2], a[4 * r + 3]))
-              : fmaxf(fmaxf(a[4 * r], a[4 * r + 1]), fmaxf(a[4 * r + 2], a[4 * r + 3]));
+              ? vmin(vmin(a[4 * r], a[4 * r + 1]), vmin(a[4 * r + 2], a[4 * r + 3]))
+              : vmax(vmax(a[4 * r], a[4 * r + 1]), vmax(a[4 * r + 2], a[4 * r + 3]));
         }
 #pragma unroll
       for (int w = G::kKB * 4; w > 1; w >>= 1)
 #pragma unroll
         for (int i = 0; i < w / 2; ++i)
-          t[i] = kNegScale ? fminf(t[i], t[i + w / 2]) : fmaxf(t[i], t[i + w / 2]);
+          t[i] = kNegScale ? vmin(t[i], t[i + w / 2]) : vmax(t[i], t[i + w / 2]);
       ext = kNegScale ? xhalf_min(t[0]) : xhalf_max(t[0]);
     } else {
-      // keys >= N hold clamped copies of row N - 1: leave them out
+      // keys >= N (zero rows) are not part of the softmax: leave them out
       float e2 = kNegScale ? INFINITY : -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key < N) e2 = kNegScale ? fminf(e2, sacc[kb][e]) : fmaxf(e2, sacc[kb][e]);
+          if (key < N) e2 = kNegScale ? vmin(e2, sacc[kb][e]) : vmax(e2, sacc[kb][e]);
         }
       ext = kNegScale ? xhalf_min(e2) : xhalf_max(e2);
     }
@@ -322,7 +348,7 @@ hipError_t launch_d(const FwdArgs& a) {
   const int n_qtiles = (a.N + kFBr - 1) / kFBr;
   const uint64_t grid = (uint64_t)n_qtiles * a.Hq * a.B;
   const float c_log2 = a.scale * 1.44269504088896341f;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, kNeg>), dim3((uint32_t)grid), dim3(kFThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_rows32_kernel<D, kNeg>), dim3((uint32_t)grid), dim3(kFThreads), 0,
                      a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.Hq,
                      a.Hkv, a.N, c_log2, n_qtiles, (uint32_t)a.n_xcd);
@@ -331,11 +357,11 @@ hipError_t launch_d(const FwdArgs& a) {
 
 }  // namespace
 
-uint64_t fwd_bf16_grid(int B, int Hq, int N) {
+uint64_t fwd_bf16_rows32_grid(int B, int Hq, int N) {
   return (uint64_t)((N + kFBr - 1) / kFBr) * Hq * B;
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a) {
+hipError_t launch_fwd_bf16_rows32(const FwdArgs& a) {
   const bool neg = a.scale < 0.0f;
   if (a.d == 128) return neg ? launch_d<128, true>(a) : launch_d<128, false>(a);
   return neg ? launch_d<64, true>(a) : launch_d<64, false>(a);

@@ -22,10 +22,19 @@ struct FwdArgs {
 };
 
 // workgroup counts (for the launch-size check)
-uint64_t fwd_bf16_grid(int B, int Hq, int N);
+uint64_t fwd_bf16_rows32_grid(int B, int Hq, int N);
+uint64_t fwd_bf16_rows64_grid(int B, int Hq, int N);
 uint64_t fwd_f32_grid(int B, int Hq, int N);
 
-hipError_t launch_fwd_bf16(const FwdArgs& a);
+// Fused bf16 forward, two kernel designs:
+//   rows32 -- one 32-row query block per wave, two workgroups per CU
+//             (head dim 64: the softmax, not LDS, bounds it there);
+//   rows64 -- two 32-row query blocks per wave sharing every K / V fragment
+//             read from LDS, software-pipelined across key tiles (head dim
+//             128, where LDS bandwidth bounds the one-block layout).
+hipError_t launch_fwd_bf16_rows32(const FwdArgs& a);
+hipError_t launch_fwd_bf16_rows64(const FwdArgs& a);
+inline bool fwd_bf16_use_rows64(int d) { return d == 128; }
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_materialized_bf16(const FwdArgs& a);
 hipError_t launch_materialized_f32(const FwdArgs& a);

@@ -17,7 +17,7 @@ import json
 import statistics
 import sys
 
-FUSED_KERNEL = "attn_fwd_bf16_kernel"
+FUSED_KERNEL = "attn_fwd_bf16_rows"
 COPY_KERNEL = "copyBuffer"
 
 
