@@ -8,7 +8,12 @@
 // an fp32 output accumulator.  S and P only ever exist in registers.
 //
 // Design for CDNA4:
-//  * 4 waves x 32 query rows.  Each wave computes S^T = K Q^T per 32-key
+//  * 4 waves x 32 query rows; at head dim 64 the kernel fits 128 VGPRs and
+//    32 KB of LDS, so four workgroups (four waves per SIMD) share a CU: at
+//    d = 64 the softmax has as many vector instructions per MFMA as at
+//    d = 128 has per two, and the other waves' instructions fill the gaps
+//    one wave leaves while it waits on its own dependencies.
+//  * Each wave computes S^T = K Q^T per 32-key
 //    block with v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the
 //    wave's Q rows resident in VGPRs as the B operand).  In that output
 //    layout a lane owns ONE query (column l % 32) and 16 of the 32 keys, so
@@ -20,8 +25,8 @@
 //    four consecutive keys of one d column.  The O^T accumulator again gives
 //    each lane one query, so the rescale by exp(m_old - m_new) is a per-lane
 //    scalar.
-//  * K and V tiles go global -> LDS directly (global_load_lds_dwordx4, no
-//    staging registers), two stages, the next tile in flight while the
+//  * K and V tiles (64 keys) go global -> LDS directly (buffer_load ... lds,
+//    no staging registers), two stages, the next tile in flight while the
 //    current one is computed.  Rows sit unpadded with their 16-byte chunks
 //    XOR-swizzled by the row index, so both the MFMA operand reads of K and
 //    the transposing reads of V are free of LDS bank conflicts.
@@ -54,7 +59,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
 struct FGeo {
-  static constexpr int kBc = (D == 128) ? 64 : 128;    // keys per tile
+  static constexpr int kBc = 64;                      // keys per tile
   static constexpr int kKB = kBc / 32;                 // 32-key blocks per tile
   static constexpr int kKSteps = D / 16;               // MFMA k-steps over d
   static constexpr int kDB = D / 32;                   // 32-wide d blocks
@@ -65,10 +70,20 @@ struct FGeo {
   static_assert(kDmaPerWave * 8 * kWave * kFWaves == kTile, "tile must split over the waves");
 };
 
-// Chunk swizzle: chunk c of row r is stored at chunk c ^ swz(r).  swz maps
-// rows r..r+7 (r % 8 == 0) onto all of 0..7, and rows r..r+3 (r % 4 == 0)
-// onto {2k + b}, which is what the two read patterns need.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Chunk swizzle: chunk c of row r is stored at chunk c ^ swz<D>(r), which
+// keeps both read patterns free of LDS bank conflicts on gfx950 (64 banks,
+// 256 bytes per cycle; measured: 4.7 cycles per ds_read_b128 of K and
+// 3.1 - 4.2 per transposing read of V, against 8.4 - 8.6 with a 3-bit swizzle):
+//  * K operand reads: lanes 0..15 read one chunk of rows r..r+15 (r % 16 ==
+//    0); the 16 (d = 128, 256-byte rows) or 2 x 8 (d = 64, two 128-byte rows
+//    per bank cycle) chunks must land on distinct banks;
+//  * transposing V reads: four rows x four 8-byte columns per 16 lanes.
+// d = 128: bits (r1 r0 r2 r3) of the row; d = 64: bits (r1 r2 r3).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 128 ? (((row & 3) << 1) | ((row >> 2) & 1) | (row & 8))
+                  : ((((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1));
+}
 
 // Issue the direct loads of one K or V tile (keys j0 .. j0 + kBc - 1) into
 // the LDS tile at byte address lds_tile.  The buffer covers only rows
@@ -116,7 +131,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 template <int D, bool kNegScale>
-__global__ __launch_bounds__(kFThreads, 2)
+__global__ __launch_bounds__(kFThreads, D == 64 ? 4 : 2)
 void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                           const __bf16* __restrict__ v, __bf16* __restrict__ o,
                           float* __restrict__ lse, int Hq, int Hkv, int N, float c_log2,
@@ -134,23 +149,26 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
 
   // direct loads: instruction i of this wave fills 16-byte chunks
   // slot .. slot + 63 of a tile; lane's chunk g = slot + lane holds logical
-  // chunk (g % kCPR) ^ swz(row) of row g / kCPR
+  // chunk (g % kCPR) ^ swz<D>(row) of row g / kCPR
   int dvoff[G::kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
     const int g = (wave * G::kDmaPerWave + i) * kWave + lane;
     const int row = g / G::kCPR;
-    const int c = (g % G::kCPR) ^ swz(row);
+    const int c = (g % G::kCPR) ^ swz<D>(row);
     dvoff[i] = (row * D + c * 8) * 2;
   }
 
   // ---- which (b, head, query tile) this workgroup owns -------------------
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
-  const int qt = (int)(logical % (uint32_t)n_qtiles);
-  uint32_t rest = logical / (uint32_t)n_qtiles;
+  // the query heads that share a K/V head are numbered fastest, then query
+  // tiles: workgroups that stream the same K/V rows at the same time run
+  // side by side on one XCD and share its L2
   const int group = Hq / Hkv;
-  const int hg = (int)(rest % (uint32_t)group);
-  rest /= (uint32_t)group;
+  const int hg = (int)(logical % (uint32_t)group);
+  uint32_t rest = logical / (uint32_t)group;
+  const int qt = (int)(rest % (uint32_t)n_qtiles);
+  rest /= (uint32_t)n_qtiles;
   const int kvh = (int)(rest % (uint32_t)Hkv);
   const int b = (int)(rest / (uint32_t)Hkv);
   const int h = kvh * group + hg;
@@ -183,18 +201,19 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
   // K operand: row kb*32 + l32, chunk 2 s + hh, swizzled by the row.
   int koff[G::kKSteps];
 #pragma unroll
-  for (int s = 0; s < G::kKSteps; ++s) koff[s] = l32 * D + (((2 * s + hh) ^ swz(l32)) * 8);
+  for (int s = 0; s < G::kKSteps; ++s) koff[s] = l32 * D + (((2 * s + hh) ^ swz<D>(l32)) * 8);
   // V^T operand (transposing read): in each 16-lane group, lane i points at
   // key (i / 4) of a 4-key run and d columns 4 (i % 4) .. +3 of the group's
   // 16 columns; it receives key run 0..3 of column (group base + i).
   const int li = lane & 15;
   const int dhalf = (lane >> 4) & 1;
   const int vrow = 4 * hh + (li >> 2);          // row within a 16-key step (plus 8 for slots 4..7)
-  int voff[G::kDB];
+  int voff[G::kDB], voff8[G::kDB];
 #pragma unroll
   for (int db = 0; db < G::kDB; ++db) {
     const int dcol = db * 32 + dhalf * 16 + 4 * (li & 3);
-    voff[db] = vrow * D + (((dcol >> 3) ^ swz(vrow)) * 8) + (dcol & 7);
+    voff[db] = vrow * D + (((dcol >> 3) ^ swz<D>(vrow)) * 8) + (dcol & 7);
+    voff8[db] = (vrow + 8) * D + (((dcol >> 3) ^ swz<D>(vrow + 8)) * 8) + (dcol & 7);
   }
 
   f32x16 oacc[G::kDB];
@@ -315,7 +334,7 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_s16x4*)(vs + rbase + voff[db]));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vs + rbase + 8 * D + voff[db]));
+              (lds_s16x4*)(vs + rbase + voff8[db]));
           const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           oacc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, a8), pf, oacc[db]);
         }

@@ -47,6 +47,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -81,10 +83,20 @@ struct FGeo {
   static_assert(2 * kDB == kUnits, "one V^T fragment per K fragment");
 };
 
-// Chunk swizzle: chunk c of row r is stored at chunk c ^ swz(r).  swz maps
-// rows r..r+7 (r % 8 == 0) onto all of 0..7, and rows r..r+3 (r % 4 == 0)
-// onto {2k + b}, which is what the two read patterns need.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Chunk swizzle: chunk c of row r is stored at chunk c ^ swz<D>(r), which
+// keeps both read patterns free of LDS bank conflicts on gfx950 (64 banks,
+// 256 bytes per cycle; measured: 4.7 cycles per ds_read_b128 of K and
+// 3.1 - 4.2 per transposing read of V, against 8.4 - 8.6 with a 3-bit swizzle):
+//  * K operand reads: lanes 0..15 read one chunk of rows r..r+15 (r % 16 ==
+//    0); the 16 (d = 128, 256-byte rows) or 2 x 8 (d = 64, two 128-byte rows
+//    per bank cycle) chunks must land on distinct banks;
+//  * transposing V reads: four rows x four 8-byte columns per 16 lanes.
+// d = 128: bits (r1 r0 r2 r3) of the row; d = 64: bits (r1 r2 r3).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 128 ? (((row & 3) << 1) | ((row >> 2) & 1) | (row & 8))
+                  : ((((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1));
+}
 
 // IEEE-754 maximum / minimum (v_maximum3_f32 / v_minimum3_f32 on gfx950):
 // unlike fmaxf they need no canonicalisation of MFMA results first.
@@ -122,9 +134,19 @@ struct WaveState {
   float m[kQB];                    // running max of the log2-scaled scores (per lane's query)
   float l[kQB];                    // this lane's part of the exp-sum
   int koff[G::kKSteps];            // LDS byte offsets of the K operand reads
-  int voff[G::kDB];                // LDS byte offsets of the V^T transposing reads
+  int voff[G::kDB];                // LDS byte offsets of the V^T transposing reads (rows +0..3)
+  int voff8[D == 128 ? 1 : G::kDB];  // the same for rows +8..11 (d = 64 only, see hi_off)
   int dvoff[G::kDma];              // byte offsets of this lane's direct loads within a tile
 };
+
+// Byte offset of the transposing V read of rows +8..11 for d block db.  For
+// d = 128, swz(r + 8) = swz(r) ^ 8 for r < 8 and bit 3 of the lane's chunk is
+// db / 2, so the offset differs from rows +0..3 by a constant.
+template <int D>
+__device__ __forceinline__ int hi_off(const WaveState<D>& w, int db) {
+  if (D == 128) return w.voff[db] + 8 * D * 2 + ((db >> 1) ? -128 : 128);
+  return w.voff8[db];
+}
 
 // The tile loads: keys [j0, j0 + kBc) of one K or V head into one LDS slot.
 // The buffer covers only rows j0 .. N-1, so rows past N read as zeros and
@@ -154,10 +176,9 @@ __device__ __forceinline__ bf16x8 lds_k(uint32_t base, int off) {
   return as_bf16x8(u);
 }
 
-template <int D>
-__device__ __forceinline__ bf16x8 lds_vt(uint32_t base, int off) {
+__device__ __forceinline__ bf16x8 lds_vt(uint32_t base, int off, int off8) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + off));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + off + 8 * D * 2));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + off8));
   const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, a8);
 }
@@ -275,11 +296,11 @@ __device__ __forceinline__ void softmax_task(int t, WaveState<D>& w, SoftmaxScra
 // ---------------------------------------------------------------------------
 // One pipeline step j (kJ4 = j mod kSlots; the slot of every LDS access is
 // a compile-time constant, which the scheduler and register allocator need):
-//   * loads K tile j + 4 and V tile j + 2 into the slots freed last step
-//     (K tile t lives in K slot t % 4, V tile t in V slot t % 4),
-//   * S^T of tile j + 1 (kQK) from K slot (j+1) % 4,
+//   * loads K tile j + S and V tile j + S - 2 into the slots freed last step
+//     (S = kSlots; K tile t lives in K slot t % S, V tile t in V slot t % S),
+//   * S^T of tile j + 1 (kQK) from K slot (j+1) % S,
 //   * the softmax of tile j,
-//   * O^T += V^T P^T of tile j - 1 (kPV) from V slot (j-1) % 4,
+//   * O^T += V^T P^T of tile j - 1 (kPV) from V slot (j-1) % S,
 //   * the O rescale of tile j (after the P V of tile j - 1),
 // then waits for K tile j + 2 and V tile j (read by step j + 1) and syncs.
 template <int D, bool kNeg, int kJ4, bool kQK, bool kPV, bool kMask>
@@ -294,8 +315,9 @@ __device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, const __bf16
   constexpr int kU = G::kUnits;
   constexpr int kAhead = 2;                  // LDS fragment reads run this many units ahead
 
-  dma_tile<D>(w.dvoff, kh, (j + 4) * kBc, N, lds + kJ4 * kTileB, wave);
-  dma_tile<D>(w.dvoff, vh, (j + 2) * kBc, N, lds + (kSlots + (kJ4 + 2) % kSlots) * kTileB, wave);
+  dma_tile<D>(w.dvoff, kh, (j + kSlots) * kBc, N, lds + kJ4 * kTileB, wave);
+  dma_tile<D>(w.dvoff, vh, (j + kSlots - 2) * kBc, N,
+              lds + (kSlots + (kJ4 + kSlots - 2) % kSlots) * kTileB, wave);
 
   SoftmaxScratch sc;
   const int valid = N - j * kBc;             // keys of tile j that exist (mask)
@@ -304,7 +326,7 @@ __device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, const __bf16
 #pragma unroll
   for (int u = 0; u < kAhead; ++u) {
     if (kQK) kf[u] = lds_k(k_rd, w.koff[u]);
-    if (kPV) vf[u] = lds_vt<D>(v_rd + (u / G::kDB) * 16 * D * 2, w.voff[u % G::kDB]);
+    if (kPV) vf[u] = lds_vt(v_rd + (u / G::kDB) * 16 * D * 2, w.voff[u % G::kDB], hi_off<D>(w, u % G::kDB));
   }
   fence();
   constexpr int kSlotsUsed = (kQK ? 2 * kU : 0) + (kPV ? 2 * kU : 0);
@@ -316,8 +338,8 @@ __device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, const __bf16
       if (u + kAhead < kU) {
         if (kQK) kf[u + kAhead] = lds_k(k_rd, w.koff[u + kAhead]);
         if (kPV)
-          vf[u + kAhead] = lds_vt<D>(v_rd + ((u + kAhead) / G::kDB) * 16 * D * 2,
-                                     w.voff[(u + kAhead) % G::kDB]);
+          vf[u + kAhead] = lds_vt(v_rd + ((u + kAhead) / G::kDB) * 16 * D * 2,
+                                  w.voff[(u + kAhead) % G::kDB], hi_off<D>(w, (u + kAhead) % G::kDB));
       }
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
@@ -357,13 +379,14 @@ __device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, const __bf16
       for (int db = 0; db < G::kDB; ++db) w.oacc[qb][db] *= sc.alpha[qb];
   }
   // K tile j+2 and V tile j (next step's reads) must have landed.  Loads
-  // issue in the order K_0 .. K_3, V_0, V_1 (prologue), then K_{t+4},
-  // V_{t+2} at step t: V_j is followed by 3 tile loads after step 0 and by
-  // 4 after any later step.
-  if (first)
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * G::kDma) : "memory");
+  // issue in the order K_0 .. K_{S-1}, V_0 .. V_{S-3} (prologue), then
+  // K_{t+S}, V_{t+S-2} at step t (S = kSlots); the later of the two, V_j,
+  // is followed by 2 (S - 2) tile loads once j >= S - 2, and by at least
+  // S - 1 before that.
+  if (j >= kSlots - 2)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kSlots - 2) * G::kDma) : "memory");
   else
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(4 * G::kDma) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kSlots - 1) * G::kDma) : "memory");
 }
 
 // O^T += V^T P^T of the last tile (V slot kJ4), outside the pipeline.
@@ -375,7 +398,7 @@ __device__ __forceinline__ void pv_last(WaveState<D>& w, uint32_t lds) {
 #pragma unroll
   for (int u = 0; u < G::kUnits; ++u) {
     const int s2 = u / G::kDB, db = u % G::kDB;
-    const bf16x8 vf = lds_vt<D>(v_rd + s2 * 16 * D * 2, w.voff[db]);
+    const bf16x8 vf = lds_vt(v_rd + s2 * 16 * D * 2, w.voff[db], hi_off<D>(w, db));
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb)
       w.oacc[qb][db] = mfma32x32x16(vf, as_bf16x8(w.p[kPar][qb][s2]), w.oacc[qb][db]);
@@ -391,6 +414,32 @@ __device__ __forceinline__ void last_step(WaveState<D>& w, uint32_t lds, const _
   else
     step<D, kNeg, kJ4, false, true, kMask>(w, lds, kh, vh, j, N, c_log2, wave, hh, j == 0);
   pv_last<D, kJ4>(w, lds);
+}
+
+// Middle steps j0 .. j0 + kSlots - 1 (j0 % kSlots == 1), stopping before
+// the last tile: every step's slots are compile-time constants.
+template <int D, bool kNeg, size_t... I>
+__device__ __forceinline__ void middle_round(WaveState<D>& w, uint32_t lds, const __bf16* kh,
+                                             const __bf16* vh, int j0, int n_tiles, int N,
+                                             float c_log2, int wave, int hh,
+                                             std::index_sequence<I...>) {
+  bool go = true;
+  ((go = go && (j0 + (int)I < n_tiles - 1) &&
+         (step<D, kNeg, (int)((I + 1) % kSlots), true, true, false>(w, lds, kh, vh, j0 + (int)I, N,
+                                                                    c_log2, wave, hh, false),
+          true)),
+   ...);
+}
+
+// The last step of tile jl, its slot picked from jl % kSlots at run time.
+template <int D, bool kNeg, bool kMask, size_t... I>
+__device__ __forceinline__ void last_round(WaveState<D>& w, uint32_t lds, const __bf16* kh,
+                                           const __bf16* vh, int jl, int N, float c_log2, int wave,
+                                           int hh, std::index_sequence<I...>) {
+  ((jl % kSlots == (int)I
+        ? (last_step<D, kNeg, (int)I, kMask>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false), 0)
+        : 0),
+   ...);
 }
 
 template <int D, bool kNeg>
@@ -412,11 +461,14 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
 
   // ---- which (b, head, query tile) this workgroup owns -------------------
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
-  const int qt = (int)(logical % (uint32_t)n_qtiles);
-  uint32_t rest = logical / (uint32_t)n_qtiles;
+  // the query heads that share a K/V head are numbered fastest, then query
+  // tiles: workgroups that stream the same K/V rows at the same time run
+  // side by side on one XCD and share its L2
   const int group = Hq / Hkv;
-  const int hg = (int)(rest % (uint32_t)group);
-  rest /= (uint32_t)group;
+  const int hg = (int)(logical % (uint32_t)group);
+  uint32_t rest = logical / (uint32_t)group;
+  const int qt = (int)(rest % (uint32_t)n_qtiles);
+  rest /= (uint32_t)n_qtiles;
   const int kvh = (int)(rest % (uint32_t)Hkv);
   const int b = (int)(rest / (uint32_t)Hkv);
   const int h = kvh * group + hg;
@@ -442,18 +494,18 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
   }
   // direct loads: instruction i of this wave fills chunks slot .. slot + 63
   // of a tile; lane's chunk g = slot + lane holds logical chunk
-  // (g % kCPR) ^ swz(row) of row g / kCPR.
+  // (g % kCPR) ^ swz<D>(row) of row g / kCPR.
 #pragma unroll
   for (int i = 0; i < G::kDma; ++i) {
     const int g = (wave * G::kDma + i) * kWave + lane;
     const int row = g / G::kCPR;
-    const int c = (g % G::kCPR) ^ swz(row);
+    const int c = (g % G::kCPR) ^ swz<D>(row);
     w.dvoff[i] = (row * D + c * 8) * 2;
   }
   // K operand: row l32, chunk 2 s + hh, swizzled by the row.
 #pragma unroll
   for (int st = 0; st < G::kKSteps; ++st)
-    w.koff[st] = (l32 * D + (((2 * st + hh) ^ swz(l32)) * 8)) * 2;
+    w.koff[st] = (l32 * D + (((2 * st + hh) ^ swz<D>(l32)) * 8)) * 2;
   // V^T operand (transposing read): in each 16-lane group, lane i points at
   // key (i / 4) of a 4-key run and d columns 4 (i % 4) .. +3 of the group's
   // 16 columns; it receives key run 0..3 of column (group base + i).
@@ -464,7 +516,8 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
 #pragma unroll
     for (int db = 0; db < G::kDB; ++db) {
       const int dcol = db * 32 + dhalf * 16 + 4 * (li & 3);
-      w.voff[db] = (vrow * D + (((dcol >> 3) ^ swz(vrow)) * 8) + (dcol & 7)) * 2;
+      w.voff[db] = (vrow * D + (((dcol >> 3) ^ swz<D>(vrow)) * 8) + (dcol & 7)) * 2;
+      if (D == 64) w.voff8[db] = ((vrow + 8) * D + (((dcol >> 3) ^ swz<D>(vrow + 8)) * 8) + (dcol & 7)) * 2;
     }
   }
 #pragma unroll
@@ -475,13 +528,14 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
     w.l[qb] = 0.0f;
   }
 
-  // ---- prologue: K tiles 0..3 and V tiles 0, 1 in flight; S of tile 0 ------
+  // ---- prologue: K tiles 0 .. S-1 and V tiles 0 .. S-3 in flight; S of tile 0
   constexpr uint32_t kTileB = G::kTile * 2;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) dma_tile<D>(w.dvoff, kh, t * kBc, N, lds + t * kTileB, wave);
-  dma_tile<D>(w.dvoff, vh, 0, N, lds + kSlots * kTileB, wave);
-  dma_tile<D>(w.dvoff, vh, kBc, N, lds + (kSlots + 1) * kTileB, wave);
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(5 * G::kDma) : "memory");   // K tile 0
+  for (int t = 0; t < kSlots; ++t) dma_tile<D>(w.dvoff, kh, t * kBc, N, lds + t * kTileB, wave);
+#pragma unroll
+  for (int t = 0; t < kSlots - 2; ++t)
+    dma_tile<D>(w.dvoff, vh, t * kBc, N, lds + (kSlots + t) * kTileB, wave);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((2 * kSlots - 3) * G::kDma) : "memory");
 #pragma unroll
   for (int st = 0; st < G::kKSteps; ++st) {
     const bf16x8 kf = lds_k(lds, w.koff[st]);
@@ -500,26 +554,14 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
     step<D, kNeg, 0, true, false, false>(w, lds, kh, vh, 0, N, c_log2, wave, hh, true);
     // middle steps 1 .. n_tiles - 2, unrolled by the ring size so every
     // slot index is a constant
-    for (int j = 1; j < n_tiles - 1; j += 4) {
-      step<D, kNeg, 1, true, true, false>(w, lds, kh, vh, j, N, c_log2, wave, hh, false);
-      if (j + 1 >= n_tiles - 1) break;
-      step<D, kNeg, 2, true, true, false>(w, lds, kh, vh, j + 1, N, c_log2, wave, hh, false);
-      if (j + 2 >= n_tiles - 1) break;
-      step<D, kNeg, 3, true, true, false>(w, lds, kh, vh, j + 2, N, c_log2, wave, hh, false);
-      if (j + 3 >= n_tiles - 1) break;
-      step<D, kNeg, 0, true, true, false>(w, lds, kh, vh, j + 3, N, c_log2, wave, hh, false);
-    }
+    for (int j = 1; j < n_tiles - 1; j += kSlots)
+      middle_round<D, kNeg>(w, lds, kh, vh, j, n_tiles, N, c_log2, wave, hh,
+                            std::make_index_sequence<kSlots>{});
     const int jl = n_tiles - 1;
-    switch ((jl % 4) + (tail ? 4 : 0)) {
-      case 0: last_step<D, kNeg, 0, false>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false); break;
-      case 1: last_step<D, kNeg, 1, false>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false); break;
-      case 2: last_step<D, kNeg, 2, false>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false); break;
-      case 3: last_step<D, kNeg, 3, false>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false); break;
-      case 4: last_step<D, kNeg, 0, true>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false); break;
-      case 5: last_step<D, kNeg, 1, true>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false); break;
-      case 6: last_step<D, kNeg, 2, true>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false); break;
-      default: last_step<D, kNeg, 3, true>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false); break;
-    }
+    if (tail)
+      last_round<D, kNeg, true>(w, lds, kh, vh, jl, N, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
+    else
+      last_round<D, kNeg, false>(w, lds, kh, vh, jl, N, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
   }
   // loads past the last tile may still be writing LDS: drain before exit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -40,11 +40,14 @@ void attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ 
   const int row_in_wg = tid >> 2;
 
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
-  const int qt = (int)(logical % (uint32_t)n_qtiles);
-  uint32_t rest = logical / (uint32_t)n_qtiles;
+  // the query heads that share a K/V head are numbered fastest, then query
+  // tiles: workgroups that stream the same K/V rows at the same time run
+  // side by side on one XCD and share its L2
   const int group = Hq / Hkv;
-  const int hg = (int)(rest % (uint32_t)group);
-  rest /= (uint32_t)group;
+  const int hg = (int)(logical % (uint32_t)group);
+  uint32_t rest = logical / (uint32_t)group;
+  const int qt = (int)(rest % (uint32_t)n_qtiles);
+  rest /= (uint32_t)n_qtiles;
   const int kvh = (int)(rest % (uint32_t)Hkv);
   const int b = (int)(rest / (uint32_t)Hkv);
   const int h = kvh * group + hg;
