@@ -71,6 +71,15 @@ def test_fused_f32_small(attn, B, Hq, Hkv, N, d):
     _check_full(attn, q, k, v, 1.0 / math.sqrt(d), torch.float32, "fused f32")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [512, 500])
+def test_many_workgroups(attn, N, d):
+    """More workgroups than the GPU holds at once (d = 128: 320 workgroups of
+    256 rows), with whole (512) and partial (500) last key tiles, GQA g = 4."""
+    q, k, v = workloads.random_inputs(1, 160, 40, N, d, torch.bfloat16, seed=13 * N + d)
+    _check_full(attn, q, k, v, 1.0 / math.sqrt(d), torch.bfloat16, "many workgroups")
+
+
 def test_single_head_fp32_workload(attn):
     w = workloads.WORKLOADS["single_head_n256_d64_f32"]
     q, k, v = workloads.make_inputs(w)
