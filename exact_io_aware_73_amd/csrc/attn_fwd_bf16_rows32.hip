@@ -85,6 +85,15 @@ __device__ __forceinline__ int swz(int row) {
                   : ((((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1));
 }
 
+// clamp(rem, 0, hi) on the scalar unit.  Written as scalar instructions so
+// the count never takes a detour through a vector register (v_med3 and
+// v_readfirstlane), which would tie the tile loads to the vector pipeline.
+__device__ __forceinline__ int srows(int rem, int hi) {
+  int r;
+  asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2" : "=&s"(r) : "s"(rem), "s"(hi) : "scc");
+  return r;
+}
+
 // Issue the direct loads of one K or V tile (keys j0 .. j0 + kBc - 1) into
 // the LDS tile at byte address lds_tile.  The buffer covers only rows
 // j0 .. N-1: rows past N read as zeros (the softmax masks them) and nothing
@@ -95,7 +104,7 @@ template <int D>
 __device__ __forceinline__ void dma_tile(const __bf16* __restrict__ head, int j0, int N,
                                          uint32_t lds_tile, int wave, const int* dvoff) {
   using G = FGeo<D>;
-  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(N - j0, G::kBc)));
+  const int rows = srows(N - j0, G::kBc);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<__bf16*>(head) + (int64_t)min(j0, N) * D, (short)0, rows * D * 2, 0x00020000);
 #pragma unroll
