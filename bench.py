@@ -106,6 +106,27 @@ def cpu_baseline(w, q, k, v, scale, budget_s: float = 12.0):
             "seconds": round(t, 3)}
 
 
+def mfma_ceiling(step_zero, stream, flops, steps: int):
+    """Context for the roofline: what dense bf16 MFMA work reaches on this
+    device with the same kind of data.  A library GEMM (8192^3, N(0,1)
+    inputs) gives the practical ceiling under the chip's power limit; the
+    fused kernel on all-zero inputs of the same shape shows how much of the
+    gap to the nominal peak is data-dependent (power) rather than code."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    with torch.cuda.stream(stream):
+        _, gemm_ms, _, _ = time_launches(lambda: torch.matmul(a, b, out=c), stream, 20, 3)
+        _, zero_ms, _, _ = time_launches(step_zero, stream, max(5, steps // 2), 3)
+    gemm = 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12
+    del a, b, c
+    return {"gemm": "torch.matmul bf16 8192x8192x8192, N(0,1) inputs", "gemm_tflops": round(gemm, 1),
+            "gemm_frac_of_peak": round(gemm / acc.PEAK_BF16_TFLOPS, 4),
+            "attn_zero_inputs_tflops": round(flops / (zero_ms * 1e-3) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +136,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the library-GEMM / zero-input context measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times): the "
                          "calibration kernel for the HBM byte counters")
@@ -186,6 +209,14 @@ def main():
                         "speedup_fused": round(m_ev / ev_mean, 2)}
         del s, p
 
+    ceiling = None
+    if not args.no_ceiling and w.dtype == "bf16":
+        qz, kz, vz = torch.zeros_like(qd), torch.zeros_like(kd), torch.zeros_like(vd)
+        ceiling = mfma_ceiling(lambda: entry(qz, kz, vz, o, lse, scale, stream), stream, flops,
+                               args.steps)
+        ceiling["attn_frac_of_gemm"] = round(achieved / ceiling["gemm_tflops"], 4)
+        del qz, kz, vz
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, scale, args.cpu_budget)
@@ -200,6 +231,7 @@ def main():
         "pct_peak": round(100 * value / peak, 2),
         "roofline": roofline,
         "materialized": materialized,
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "kernel_source_sha": kernel_source_hash(),
     }
