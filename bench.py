@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--split", type=int, default=0,
+                    help="time the split-KV entry point (attn_fwd_split) with this many key "
+                         "ranges instead of attn_fwd (bf16 only)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the library-GEMM / zero-input context measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -170,6 +173,14 @@ def main():
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
     entry = attn.attn_fwd if w.dtype == "bf16" else attn.attn_fwd_f32
+    if args.split:
+        if w.dtype != "bf16":
+            sys.exit("--split takes a bf16 workload")
+        ws = torch.empty(attn.attn_fwd_split_workspace_bytes(w.B, w.Hq, w.N, w.d, args.split),
+                         dtype=torch.uint8, device="cuda")
+
+        def entry(q_, k_, v_, o_, lse_, scale_, stream_):
+            attn.attn_fwd_split(q_, k_, v_, o_, lse_, ws, args.split, scale_, stream_)
 
     def step():
         entry(qd, kd, vd, o, lse, scale, stream)
@@ -182,7 +193,8 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     peak = acc.PEAK_BF16_TFLOPS if w.dtype == "bf16" else acc.PEAK_FP32_VECTOR_TFLOPS
     achieved = flops / (ev_mean * 1e-3) / 1e12
-    traffic = traffic_from_profiles(w.name, flops)
+    # the byte counters are taken on attn_fwd; the split path has its own kernels
+    traffic = None if args.split else traffic_from_profiles(w.name, flops)
     roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel_ms_mean": round(ev_mean, 4),
@@ -227,7 +239,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "io_dtype": w.dtype, "parallelism": "none", "inputs": "iid N(0,1), seeded"},
+                   "io_dtype": w.dtype, "parallelism": "none", "inputs": "iid N(0,1), seeded",
+                   "entry": f"attn_fwd_split(n_split={args.split})" if args.split else
+                            ("attn_fwd" if w.dtype == "bf16" else "attn_fwd_f32")},
         "pct_peak": round(100 * value / peak, 2),
         "roofline": roofline,
         "materialized": materialized,

@@ -10,9 +10,12 @@ Entry points carry the C names and take tensors instead of raw pointers:
     attn_fwd_f32(q, k, v, o, lse, scale, stream=None)             fp32
     attn_fwd_materialized(q, k, v, o, lse, s, p, scale, stream=None)
     attn_fwd_materialized_f32(q, k, v, o, lse, s, p, scale, stream=None)
+    attn_fwd_split(q, k, v, o, lse, workspace, n_split, scale, stream=None)   bf16
+    attn_fwd_split_workspace_bytes(B, Hq, N, d, n_split)
     attn_strerror(status)
 
-plus ``fwd`` / ``fwd_materialized``, which allocate the outputs and pick the
+plus ``fwd`` / ``fwd_materialized`` / ``fwd_split``, which allocate the outputs
+(and the split path's workspace) and pick the
 entry point by dtype.  q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous
 CUDA (HIP) tensors.  Argument errors raise ValueError, launch errors
 RuntimeError.
@@ -41,11 +44,18 @@ _lib.attn_fwd_materialized.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _
 _lib.attn_fwd_materialized_f32.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]
 for _fn in ("attn_fwd", "attn_fwd_f32", "attn_fwd_materialized", "attn_fwd_materialized_f32"):
     getattr(_lib, _fn).restype = _I
+_U64 = ctypes.c_ulonglong
+_lib.attn_fwd_split.argtypes = [_P, _P, _P, _P, _P, _P, _U64, _I, _I, _I, _I, _I, _I, _F, _P]
+_lib.attn_fwd_split.restype = _I
+_lib.attn_fwd_split_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+_lib.attn_fwd_split_workspace_bytes.restype = _U64
 _lib.attn_strerror.argtypes = [_I]
 _lib.attn_strerror.restype = ctypes.c_char_p
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_GQA, ATTN_ERR_HEADDIM = 0, 1, 2, 3, 4
 ATTN_ERR_SCALE, ATTN_ERR_ALIGN, ATTN_ERR_ALIAS, ATTN_ERR_HIP = 5, 6, 7, 8
+ATTN_ERR_SPLIT, ATTN_ERR_WORKSPACE = 9, 10
+ATTN_MAX_SPLIT = 64
 
 
 def attn_strerror(status: int) -> str:
@@ -133,6 +143,34 @@ def attn_fwd_materialized_f32(q, k, v, o, lse, s, p, scale, stream=None):
     _call("attn_fwd_materialized_f32", torch.float32, q, k, v, o, lse, s, p, scale, stream)
 
 
+def attn_fwd_split_workspace_bytes(B, Hq, N, d, n_split) -> int:
+    """Workspace bytes attn_fwd_split needs (0 for arguments it would reject)."""
+    return int(_lib.attn_fwd_split_workspace_bytes(int(B), int(Hq), int(N), int(d), int(n_split)))
+
+
+def attn_fwd_split(q, k, v, o, lse, workspace, n_split, scale, stream=None):
+    """Split-KV forward, bf16 I/O (C: attn_fwd_split); workspace: a contiguous
+    device tensor of at least attn_fwd_split_workspace_bytes(...) bytes."""
+    fn_name = "attn_fwd_split"
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
+                        ("o", o, torch.bfloat16), ("lse", lse, torch.float32)):
+        if t.dtype != dt:
+            raise ValueError(f"{fn_name}: {name} must be {dt}, got {t.dtype}")
+        if t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{fn_name}: {name} must be contiguous on {q.device}")
+    if o.shape != q.shape or lse.shape != (B, Hq, N):
+        raise ValueError(f"{fn_name}: o must be {tuple(q.shape)} and lse {(B, Hq, N)}")
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError(f"{fn_name}: workspace must be contiguous on {q.device}")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = _lib.attn_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                                 ws_bytes, int(n_split), B, Hq, Hkv, N, d,
+                                 ctypes.c_float(float(scale)), _stream_handle(stream, q.device))
+    _raise(st, fn_name)
+
+
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
@@ -165,3 +203,18 @@ def fwd_materialized(q, k, v, scale=None, stream=None):
     else:
         raise ValueError(f"unsupported dtype {q.dtype}; use bfloat16 or float32")
     return o, lse, s, p
+
+
+def fwd_split(q, k, v, n_split, scale=None, stream=None):
+    """(o, lse) through the split-KV path (bf16); allocates its workspace."""
+    B, Hq, _, N, d = _dims(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError(f"the split-KV path takes bfloat16, got {q.dtype}")
+    need = attn_fwd_split_workspace_bytes(B, Hq, N, d, n_split)
+    if need == 0:
+        raise ValueError(f"attn_fwd_split: invalid arguments (n_split={n_split}, d={d})")
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    attn_fwd_split(q, k, v, o, lse, ws, n_split, _scale(scale, d), stream)
+    return o, lse

@@ -125,6 +125,48 @@ int materialized_impl(bool bf16, const void* q, const void* k, const void* v, vo
   return to_status(bf16 ? attn::launch_materialized_bf16(a) : attn::launch_materialized_f32(a));
 }
 
+// Workspace of the split-KV path: fp32 partial O and lse per range and row.
+uint64_t split_ws_bytes(int B, int Hq, int N, int d, int n_split) {
+  return (uint64_t)n_split * B * Hq * (uint64_t)N * (uint64_t)(d + 1) * 4u;
+}
+
+int split_impl(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+               uint64_t ws_bytes, int n_split, int B, int Hq, int Hkv, int N, int d, float scale,
+               void* stream) {
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (n_split < 1 || n_split > ATTN_MAX_SPLIT) return ATTN_ERR_SPLIT;
+  const uint64_t chunk = attn::split_chunk_keys(N, n_split);
+  const int n_eff = (int)(((uint64_t)N + chunk - 1) / chunk);   // non-empty ranges
+  const uint64_t rows = (uint64_t)B * Hq * N;
+  if (attn::fwd_bf16_rows64_grid(B, Hq, N) * n_eff > kMaxWorkgroups ||
+      rows * (uint64_t)(d / 8) / 256 + 1 > kMaxWorkgroups)
+    return ATTN_ERR_SHAPE;
+  const uint64_t need = split_ws_bytes(B, Hq, N, d, n_split);
+  if (!ws || !aligned(ws, 16) || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+  st = check_alias(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, 2, 0);
+  if (st != ATTN_OK) return st;
+  {
+    auto rng = [](const void* ptr, uint64_t bytes) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+      return Range{lo, lo + (uintptr_t)bytes};
+    };
+    const uint64_t qo = rows * d * 2, kv = (uint64_t)B * Hkv * N * d * 2;
+    const Range w = rng(ws, need);
+    const Range other[5] = {rng(q, qo), rng(k, kv), rng(v, kv), rng(o, qo), rng(lse, rows * 4)};
+    for (const Range& r : other)
+      if (overlap(w, r)) return ATTN_ERR_ALIAS;
+  }
+  attn::FwdArgs a = make_args(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, scale, stream);
+  a.n_split = n_eff;
+  a.chunk_keys = (int)chunk;
+  a.part_o = static_cast<float*>(ws);
+  a.part_lse = static_cast<float*>(ws) + (uint64_t)n_eff * rows * d;
+  st = to_status(attn::launch_fwd_bf16_split(a));
+  if (st != ATTN_OK) return st;
+  return to_status(attn::launch_split_merge_bf16(a));
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,6 +209,25 @@ ATTN_API int attn_fwd_materialized_f32(const float* q, const float* k, const flo
   }
 }
 
+ATTN_API int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                            void* workspace, unsigned long long workspace_bytes, int n_split,
+                            int B, int Hq, int Hkv, int N, int d, float scale, void* stream) {
+  try {
+    return split_impl(q, k, v, o, lse, workspace, workspace_bytes, n_split, B, Hq, Hkv, N, d,
+                      scale, stream);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+ATTN_API unsigned long long attn_fwd_split_workspace_bytes(int B, int Hq, int N, int d,
+                                                           int n_split) {
+  if (B < 1 || Hq < 1 || N < 1 || (d != 64 && d != 128) || n_split < 1 ||
+      n_split > ATTN_MAX_SPLIT)
+    return 0;
+  return split_ws_bytes(B, Hq, N, d, n_split);
+}
+
 ATTN_API const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";
@@ -178,6 +239,8 @@ ATTN_API const char* attn_strerror(int status) {
     case ATTN_ERR_ALIGN: return "q/k/v/o/s/p must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case ATTN_ERR_SPLIT: return "n_split must be in [1, ATTN_MAX_SPLIT]";
+    case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned or too small";
     default: return "unknown status";
   }
 }

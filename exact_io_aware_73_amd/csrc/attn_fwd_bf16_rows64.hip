@@ -450,12 +450,18 @@ __device__ __forceinline__ void last_round(WaveState<D>& w, uint32_t lds, const 
    ...);
 }
 
-template <int D, bool kNeg>
-__global__ __launch_bounds__(kFThreads, 1)
-void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                          const __bf16* __restrict__ v, __bf16* __restrict__ o,
-                          float* __restrict__ lse, int Hq, int Hkv, int N, float c_log2,
-                          int n_qtiles, uint32_t n_xcd) {
+// kSplit: the workgroup covers one of n_split contiguous key ranges of
+// chunk_keys keys (whole tiles) and writes its partial result -- O of its
+// keys, normalised by their own exp-sum, and their log-sum-exp -- as fp32 to
+// part_o / part_lse; attn_split_merge combines the ranges.
+template <int D, bool kNeg, bool kSplit>
+__device__ __forceinline__ void rows64_body(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                            const __bf16* __restrict__ v, __bf16* __restrict__ o,
+                                            float* __restrict__ lse, int Hq, int Hkv, int N,
+                                            float c_log2, int n_qtiles, uint32_t n_xcd,
+                                            int n_split, int chunk_keys, int64_t n_rows,
+                                            float* __restrict__ part_o,
+                                            float* __restrict__ part_lse) {
   using G = FGeo<D>;
   // K slots then V slots, kBc x D bf16 each
   __shared__ __align__(16) __bf16 smem[2 * kSlots * G::kTile];
@@ -477,15 +483,24 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
   uint32_t rest = logical / (uint32_t)group;
   const int qt = (int)(rest % (uint32_t)n_qtiles);
   rest /= (uint32_t)n_qtiles;
+  // split: the key range next (all query tiles of one range run side by side)
+  int split = 0;
+  if (kSplit) {
+    split = (int)(rest % (uint32_t)n_split);
+    rest /= (uint32_t)n_split;
+  }
   const int kvh = (int)(rest % (uint32_t)Hkv);
   const int b = (int)(rest / (uint32_t)Hkv);
   const int h = kvh * group + hg;
 
   const int64_t head_q = ((int64_t)b * Hq + h) * (int64_t)N;     // row index base
   const int64_t head_kv = ((int64_t)b * Hkv + kvh) * (int64_t)N;
-  const __bf16* kh = k + head_kv * D;
-  const __bf16* vh = v + head_kv * D;
-  const int n_tiles = (N + kBc - 1) / kBc;
+  // this workgroup's keys: all N, or the range [k0, k0 + Nk) of its split
+  const int k0 = kSplit ? split * chunk_keys : 0;
+  const int Nk = kSplit ? min(chunk_keys, N - k0) : N;
+  const __bf16* kh = k + (head_kv + k0) * D;
+  const __bf16* vh = v + (head_kv + k0) * D;
+  const int n_tiles = (Nk + kBc - 1) / kBc;
 
   WaveState<D> w;
   // ---- Q^T fragments: lane holds d = 16 s + 8 hh .. +7 of its queries -----
@@ -539,10 +554,10 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
   // ---- prologue: K tiles 0 .. S-1 and V tiles 0 .. S-3 in flight; S of tile 0
   constexpr uint32_t kTileB = G::kTile * 2;
 #pragma unroll
-  for (int t = 0; t < kSlots; ++t) dma_tile<D>(w.dvoff, kh, t * kBc, N, lds + t * kTileB, wave);
+  for (int t = 0; t < kSlots; ++t) dma_tile<D>(w.dvoff, kh, t * kBc, Nk, lds + t * kTileB, wave);
 #pragma unroll
   for (int t = 0; t < kSlots - 2; ++t)
-    dma_tile<D>(w.dvoff, vh, t * kBc, N, lds + (kSlots + t) * kTileB, wave);
+    dma_tile<D>(w.dvoff, vh, t * kBc, Nk, lds + (kSlots + t) * kTileB, wave);
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((2 * kSlots - 3) * G::kDma) : "memory");
 #pragma unroll
   for (int st = 0; st < G::kKSteps; ++st) {
@@ -554,22 +569,22 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
   // every wave has read K slot 0 before step 0 reloads it
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  const bool tail = (N % kBc) != 0;
+  const bool tail = (Nk % kBc) != 0;
   if (n_tiles == 1) {
-    if (tail) last_step<D, kNeg, 0, true>(w, lds, kh, vh, 0, N, c_log2, wave, hh, true);
-    else last_step<D, kNeg, 0, false>(w, lds, kh, vh, 0, N, c_log2, wave, hh, true);
+    if (tail) last_step<D, kNeg, 0, true>(w, lds, kh, vh, 0, Nk, c_log2, wave, hh, true);
+    else last_step<D, kNeg, 0, false>(w, lds, kh, vh, 0, Nk, c_log2, wave, hh, true);
   } else {
-    step<D, kNeg, 0, true, false, false>(w, lds, kh, vh, 0, N, c_log2, wave, hh, true);
+    step<D, kNeg, 0, true, false, false>(w, lds, kh, vh, 0, Nk, c_log2, wave, hh, true);
     // middle steps 1 .. n_tiles - 2, unrolled by the ring size so every
     // slot index is a constant
     for (int j = 1; j < n_tiles - 1; j += kSlots)
-      middle_round<D, kNeg>(w, lds, kh, vh, j, n_tiles, N, c_log2, wave, hh,
+      middle_round<D, kNeg>(w, lds, kh, vh, j, n_tiles, Nk, c_log2, wave, hh,
                             std::make_index_sequence<kSlots>{});
     const int jl = n_tiles - 1;
     if (tail)
-      last_round<D, kNeg, true>(w, lds, kh, vh, jl, N, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
+      last_round<D, kNeg, true>(w, lds, kh, vh, jl, Nk, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
     else
-      last_round<D, kNeg, false>(w, lds, kh, vh, jl, N, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
+      last_round<D, kNeg, false>(w, lds, kh, vh, jl, Nk, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
   }
   // loads past the last tile may still be writing LDS: drain before exit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -579,7 +594,23 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
   for (int qb = 0; qb < kQB; ++qb) {
     const int qrow = qt * kFBr + wave * kFRows + qb * 32 + l32;
     const float l_tot = xhalf_sum(w.l[qb]);
-    if (qrow < N) {
+    if (kSplit && qrow < N) {
+      // partial result of this key range: O / l in fp32 and its lse
+      const float inv = 1.0f / l_tot;
+      const int64_t prow = (int64_t)split * n_rows + head_q + qrow;
+      float* orow = part_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < G::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          f32x4 ov;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = w.oacc[qb][db][4 * r + i] * inv;
+          *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * r + 4 * hh) = ov;
+        }
+      if (hh == 0) part_lse[prow] = (w.m[qb] + log2_fast(l_tot)) * 0.69314718055994531f;
+    }
+    if (!kSplit && qrow < N) {
       const float inv = 1.0f / l_tot;
       __bf16* orow = o + (head_q + qrow) * D;
 #pragma unroll
@@ -597,14 +628,44 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
 }
 
 template <int D, bool kNeg>
+__global__ __launch_bounds__(kFThreads, 1)
+void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                          const __bf16* __restrict__ v, __bf16* __restrict__ o,
+                          float* __restrict__ lse, int Hq, int Hkv, int N, float c_log2,
+                          int n_qtiles, uint32_t n_xcd) {
+  rows64_body<D, kNeg, false>(q, k, v, o, lse, Hq, Hkv, N, c_log2, n_qtiles, n_xcd, 1, N, 0,
+                              nullptr, nullptr);
+}
+
+template <int D, bool kNeg>
+__global__ __launch_bounds__(kFThreads, 1)
+void attn_fwd_bf16_rows64_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                const __bf16* __restrict__ v, int Hq, int Hkv, int N,
+                                float c_log2, int n_qtiles, uint32_t n_xcd, int n_split,
+                                int chunk_keys, int64_t n_rows, float* __restrict__ part_o,
+                                float* __restrict__ part_lse) {
+  rows64_body<D, kNeg, true>(q, k, v, nullptr, nullptr, Hq, Hkv, N, c_log2, n_qtiles, n_xcd,
+                             n_split, chunk_keys, n_rows, part_o, part_lse);
+}
+
+template <int D, bool kNeg, bool kSplit>
 hipError_t launch_d(const FwdArgs& a) {
   const int n_qtiles = (a.N + kFBr - 1) / kFBr;
-  const uint64_t grid = (uint64_t)n_qtiles * a.Hq * a.B;
+  const int n_split = kSplit ? a.n_split : 1;
+  const uint64_t grid = (uint64_t)n_qtiles * a.Hq * a.B * n_split;
   const float c_log2 = a.scale * 1.44269504088896341f;
-  hipLaunchKernelGGL((attn_fwd_bf16_rows64_kernel<D, kNeg>), dim3((uint32_t)grid), dim3(kFThreads), 0,
-                     a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.Hq,
-                     a.Hkv, a.N, c_log2, n_qtiles, (uint32_t)a.n_xcd);
+  if (kSplit)
+    hipLaunchKernelGGL((attn_fwd_bf16_rows64_split_kernel<D, kNeg>), dim3((uint32_t)grid),
+                       dim3(kFThreads), 0, a.stream, static_cast<const __bf16*>(a.q),
+                       static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v), a.Hq,
+                       a.Hkv, a.N, c_log2, n_qtiles, (uint32_t)a.n_xcd, n_split, a.chunk_keys,
+                       (int64_t)a.B * a.Hq * a.N, a.part_o, a.part_lse);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_rows64_kernel<D, kNeg>), dim3((uint32_t)grid),
+                       dim3(kFThreads), 0, a.stream, static_cast<const __bf16*>(a.q),
+                       static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
+                       static_cast<__bf16*>(a.o), a.lse, a.Hq, a.Hkv, a.N, c_log2, n_qtiles,
+                       (uint32_t)a.n_xcd);
   return hipGetLastError();
 }
 
@@ -616,8 +677,20 @@ uint64_t fwd_bf16_rows64_grid(int B, int Hq, int N) {
 
 hipError_t launch_fwd_bf16_rows64(const FwdArgs& a) {
   const bool neg = a.scale < 0.0f;
-  if (a.d == 128) return neg ? launch_d<128, true>(a) : launch_d<128, false>(a);
-  return neg ? launch_d<64, true>(a) : launch_d<64, false>(a);
+  if (a.d == 128) return neg ? launch_d<128, true, false>(a) : launch_d<128, false, false>(a);
+  return neg ? launch_d<64, true, false>(a) : launch_d<64, false, false>(a);
+}
+
+uint64_t split_chunk_keys(int N, int n_split) {
+  const int n_tiles = (N + kBc - 1) / kBc;
+  const int per = (n_tiles + n_split - 1) / n_split;   // whole tiles per range
+  return (uint64_t)per * kBc;
+}
+
+hipError_t launch_fwd_bf16_split(const FwdArgs& a) {
+  const bool neg = a.scale < 0.0f;
+  if (a.d == 128) return neg ? launch_d<128, true, true>(a) : launch_d<128, false, true>(a);
+  return neg ? launch_d<64, true, true>(a) : launch_d<64, false, true>(a);
 }
 
 }  // namespace attn

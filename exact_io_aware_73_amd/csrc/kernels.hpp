@@ -18,6 +18,12 @@ struct FwdArgs {
   int B, Hq, Hkv, N, d;
   float scale;
   int n_xcd;
+  // split-KV path only: the key ranges, their length (whole tiles) and the
+  // fp32 partial results [n_split][B*Hq*N][d] and [n_split][B*Hq*N]
+  int n_split = 1;
+  int chunk_keys = 0;
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
   hipStream_t stream;
 };
 
@@ -36,6 +42,14 @@ hipError_t launch_fwd_bf16_rows32(const FwdArgs& a);
 hipError_t launch_fwd_bf16_rows64(const FwdArgs& a);
 inline bool fwd_bf16_use_rows64(int d) { return d == 128; }
 hipError_t launch_fwd_f32(const FwdArgs& a);
+
+// Split-KV forward (bf16): the rows64 kernel over key ranges of
+// split_chunk_keys(N, n_split) keys into part_o / part_lse, then the merge
+// of the ranges into o / lse.  The number of non-empty ranges is
+// ceil(N / chunk_keys), which may be below the requested n_split.
+uint64_t split_chunk_keys(int N, int n_split);
+hipError_t launch_fwd_bf16_split(const FwdArgs& a);
+hipError_t launch_split_merge_bf16(const FwdArgs& a);
 hipError_t launch_materialized_bf16(const FwdArgs& a);
 hipError_t launch_materialized_f32(const FwdArgs& a);
 

@@ -64,8 +64,13 @@ typedef enum {
   ATTN_ERR_SCALE = 5,    /* scale is NaN or infinite */
   ATTN_ERR_ALIGN = 6,    /* q/k/v/o/s/p not 16-byte aligned, or lse not 4-byte aligned */
   ATTN_ERR_ALIAS = 7,    /* an output overlaps an input or another output */
-  ATTN_ERR_HIP = 8       /* the HIP runtime reported an error at launch */
+  ATTN_ERR_HIP = 8,      /* the HIP runtime reported an error at launch */
+  ATTN_ERR_SPLIT = 9,    /* n_split outside [1, ATTN_MAX_SPLIT] */
+  ATTN_ERR_WORKSPACE = 10 /* workspace NULL, misaligned or smaller than required */
 } attn_status_t;
+
+/* Largest number of key ranges the split-KV entry point accepts. */
+#define ATTN_MAX_SPLIT 64
 
 /*
  * attn_fwd -- fused tiled forward, bfloat16 I/O, float32 accumulation.
@@ -115,6 +120,40 @@ ATTN_API int attn_fwd_materialized_f32(const float* q, const float* k, const flo
                                        float* lse, float* s, float* p,
                                        int B, int Hq, int Hkv, int N, int d, float scale,
                                        void* stream);
+
+/*
+ * attn_fwd_split -- the fused forward with every head's keys cut into up to
+ * n_split contiguous ranges of whole 32-key tiles, each range handled by its
+ * own workgroups (for heads too few or too long to fill the GPU: one head of
+ * 32768 rows gives 128 workgroups for 256 compute units).  Each range
+ * writes its partial result -- O of its keys normalised by their own
+ * exp-sum, and the log-sum-exp lse_r of its scores -- to the workspace; a
+ * second kernel merges the ranges of every row by the online-softmax
+ * rescale rule (blog "attention 的显存线性化", section 三):
+ *   lse = ln sum_r exp(lse_r),   O = sum_r exp(lse_r - lse) * O_r.
+ * Exact up to rounding, like attn_fwd; deterministic.
+ *
+ * bf16 q, k, v, o; float32 lse; same layouts as attn_fwd.  n_split in
+ * [1, ATTN_MAX_SPLIT]; ranges hold ceil(ceil(N/32) / n_split) tiles, so
+ * fewer than n_split ranges run when N is short.
+ *
+ * workspace: a DEVICE buffer owned by the caller, 16-byte aligned, of at
+ * least attn_fwd_split_workspace_bytes(B, Hq, N, d, n_split) bytes; its
+ * contents on entry do not matter and on return are unspecified.  It must
+ * not overlap the inputs or outputs.  Two calls that share a workspace must
+ * be ordered (same stream).
+ */
+ATTN_API int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                            void* workspace, unsigned long long workspace_bytes, int n_split,
+                            int B, int Hq, int Hkv, int N, int d, float scale, void* stream);
+
+/*
+ * attn_fwd_split_workspace_bytes -- workspace attn_fwd_split needs:
+ * n_split * B * Hq * N * (d + 1) * 4 bytes (fp32 partial O and lse per
+ * range and row).  0 for arguments attn_fwd_split would reject.
+ */
+ATTN_API unsigned long long attn_fwd_split_workspace_bytes(int B, int Hq, int N, int d,
+                                                           int n_split);
 
 /* attn_strerror -- a static, NUL-terminated description of a status code. */
 ATTN_API const char* attn_strerror(int status);

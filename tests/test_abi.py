@@ -32,6 +32,9 @@ def lib():
     l.attn_fwd_f32.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P]
     l.attn_fwd_materialized.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, P]
     l.attn_fwd_materialized_f32.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, P]
+    l.attn_fwd_split.argtypes = [P, P, P, P, P, P, ctypes.c_ulonglong, I, I, I, I, I, I, F, P]
+    l.attn_fwd_split_workspace_bytes.argtypes = [I, I, I, I, I]
+    l.attn_fwd_split_workspace_bytes.restype = ctypes.c_ulonglong
     l.attn_strerror.argtypes = [I]
     l.attn_strerror.restype = ctypes.c_char_p
     return l
@@ -39,7 +42,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert set(_declared()) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_materialized",
-                                "attn_fwd_materialized_f32", "attn_strerror"}
+                                "attn_fwd_materialized_f32", "attn_fwd_split",
+                                "attn_fwd_split_workspace_bytes", "attn_strerror"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -111,3 +115,41 @@ def test_python_binding_signatures_match_header():
     src = open(os.path.join(ROOT, "exact_io_aware_73_amd", "attn.py")).read()
     for name in _declared():
         assert re.search(rf"^def {name}\(", src, re.M), name
+
+
+# ---------------------------------------------------------------------------
+# split-KV entry point
+W = A * 9     # fake workspace address, apart from the others
+
+
+def _split(lib, q=Q, k=K, v=V, o=O, lse=L, ws=W, ws_bytes=1 << 40, n_split=4, B=1, Hq=2, Hkv=1,
+           N=16, d=64, scale=0.125):
+    return lib.attn_fwd_split(q, k, v, o, lse, ws, ws_bytes, n_split, B, Hq, Hkv, N, d,
+                              ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("B,Hq,N,d,S", [(1, 1, 1, 64, 1), (2, 8, 1000, 128, 4), (1, 1, 32768, 128, 64),
+                                         (3, 5, 17, 64, 7)])
+def test_split_workspace_bytes(lib, B, Hq, N, d, S):
+    assert lib.attn_fwd_split_workspace_bytes(B, Hq, N, d, S) == S * B * Hq * N * (d + 1) * 4
+
+
+@pytest.mark.parametrize("args", [(0, 1, 16, 64, 2), (1, 0, 16, 64, 2), (1, 1, 0, 64, 2),
+                                  (1, 1, 16, 96, 2), (1, 1, 16, 64, 0), (1, 1, 16, 64, 65)])
+def test_split_workspace_bytes_rejects(lib, args):
+    assert lib.attn_fwd_split_workspace_bytes(*args) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_split=0), "ATTN_ERR_SPLIT"), (dict(n_split=65), "ATTN_ERR_SPLIT"),
+    (dict(n_split=-1), "ATTN_ERR_SPLIT"),
+    (dict(ws=None), "ATTN_ERR_WORKSPACE"), (dict(ws=W + 8), "ATTN_ERR_WORKSPACE"),
+    (dict(ws_bytes=4 * 2 * 16 * 65 * 4 - 1), "ATTN_ERR_WORKSPACE"),
+    (dict(ws=Q), "ATTN_ERR_ALIAS"), (dict(ws=O - 64), "ATTN_ERR_ALIAS"), (dict(ws=L), "ATTN_ERR_ALIAS"),
+    (dict(q=None), "ATTN_ERR_NULL"), (dict(o=None), "ATTN_ERR_NULL"),
+    (dict(Hq=3, Hkv=2), "ATTN_ERR_GQA"), (dict(d=32), "ATTN_ERR_HEADDIM"),
+    (dict(scale=math.nan), "ATTN_ERR_SCALE"), (dict(N=0), "ATTN_ERR_SHAPE"),
+    (dict(o=Q), "ATTN_ERR_ALIAS"), (dict(q=Q + 8), "ATTN_ERR_ALIGN"),
+])
+def test_split_rejects(lib, kw, code):
+    assert _split(lib, **kw) == _status_codes()[code]

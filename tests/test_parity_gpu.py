@@ -80,6 +80,66 @@ def test_many_workgroups(attn, N, d):
     _check_full(attn, q, k, v, 1.0 / math.sqrt(d), torch.bfloat16, "many workgroups")
 
 
+# ---------------------------------------------------------------------------
+# split-KV path: key ranges per workgroup, partial (O, lse) merged
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,n_split", [(1, 1), (1, 4), (31, 2), (32, 2), (33, 2), (100, 3),
+                                        (257, 4), (1000, 7), (1000, 64)])
+@pytest.mark.parametrize("B,Hq,Hkv", [(1, 1, 1), (2, 8, 2)])
+def test_split_small(attn, B, Hq, Hkv, N, n_split, d):
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=17 * N + d + n_split)
+    scale = 1.0 / math.sqrt(d)
+    _say(f"[parity] split n_split={n_split} q={tuple(q.shape)} k={tuple(k.shape)}")
+    o, lse = attn.fwd_split(q.cuda(), k.cuda(), v.cuda(), n_split, scale)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = oracle.attention_ref(workloads.to_f64(q), workloads.to_f64(k),
+                                          workloads.to_f64(v), scale)
+    r = compare(workloads.to_f64(o.cpu()), lse.cpu().numpy(), O_ref, lse_ref, "bf16")
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 3.0])
+def test_split_scales(attn, scale):
+    q, k, v = workloads.random_inputs(1, 4, 2, 300, 128, torch.bfloat16, seed=98)
+    o, lse = attn.fwd_split(q.cuda(), k.cuda(), v.cuda(), 3, scale)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = oracle.attention_ref(workloads.to_f64(q), workloads.to_f64(k),
+                                          workloads.to_f64(v), scale)
+    r = compare(workloads.to_f64(o.cpu()), lse.cpu().numpy(), O_ref, lse_ref, "bf16")
+    assert r["ok"], r
+
+
+def test_split_single_long_head(attn):
+    """One head of 32768 rows (128 workgroups unsplit): four key ranges,
+    sampled rows against the oracle, every row against the unsplit path."""
+    q, k, v = workloads.random_inputs(1, 1, 1, 32768, 128, torch.bfloat16, seed=21)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    _say("[parity] split single head N=32768 n_split=4")
+    o1, l1 = attn.fwd_split(qd, kd, vd, 4)
+    o2, l2 = attn.fwd_split(qd, kd, vd, 4)
+    o0, l0 = attn.fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "not deterministic"
+    # both paths approximate the same exact result within the bf16 bound
+    assert (o1.float() - o0.float()).abs().max().item() <= 2e-2
+    assert (l1 - l0).abs().max().item() <= 2e-3
+    r = check_sampled(q, k, v, o1.cpu(), l1.cpu(), 1 / math.sqrt(128), "bf16", seed=5)
+    _say(f"[parity] split single head: {r}")
+
+
+def test_python_split_rejects(attn):
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        attn.fwd_split(q, q, q, 0)
+    with pytest.raises(ValueError):
+        attn.fwd_split(q, q, q, attn.ATTN_MAX_SPLIT + 1)
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 2, 8, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")   # far too small
+    with pytest.raises(ValueError):
+        attn.attn_fwd_split(q, q, q, o, lse, ws, 2, 0.125)
+
+
 def test_single_head_fp32_workload(attn):
     w = workloads.WORKLOADS["single_head_n256_d64_f32"]
     q, k, v = workloads.make_inputs(w)

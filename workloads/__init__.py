@@ -64,6 +64,9 @@ WORKLOADS = {
                  description="as above, 1% of K rows scaled by 8 to stress the running-max rescale"),
         Workload("long_context_b1_h8_n32768_d128", 1, 8, 8, 32768, 128, "bf16", 5000,
                  description="long-context attention forward; S+P would be 4.3 GB per head"),
+        Workload("one_head_b1_h1_n32768_d128", 1, 1, 1, 32768, 128, "bf16", 6000,
+                 description="one long head: 128 query tiles of 256 rows for 256 compute "
+                             "units, the case the split-KV path is for"),
     ]
 }
 
