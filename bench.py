@@ -32,6 +32,7 @@ from exact_io_aware_73_amd import accounting as acc  # noqa: E402
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak; HBM bytes vs Q/K/V/O min"
 KERNEL_SOURCES = ["exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows32.hip",
                   "exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows64.hip",
+                  "exact_io_aware_73_amd/csrc/rows64_pipeline.hpp",
                   "exact_io_aware_73_amd/csrc/attn_fwd_f32.hip",
                   "exact_io_aware_73_amd/csrc/device_common.hpp",
                   "exact_io_aware_73_amd/build.py"]

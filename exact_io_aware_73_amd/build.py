@@ -34,6 +34,7 @@ CFLAGS = [
 # instead of moving every score through the accumulation registers.
 FILE_FLAGS = {
     "attn_fwd_bf16_rows64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attn_fwd_bf16_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
