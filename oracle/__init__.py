@@ -1,4 +1,4 @@
-"""CPU oracle for exact attention forward (test infrastructure only).
+"""CPU oracle for exact attention forward and its gradients (test infrastructure only).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
 ``cpu_baseline`` leg may import this package.  The GPU product path never
@@ -7,7 +7,8 @@ does, and this package never imports the GPU path.
 from .attention import (attention_head, attention_ref, attention_ref_rows,
                         attention_ref_sp, default_scale, head_scores, kv_head,
                         softmax_rows)
+from .backward import attention_bwd_head, attention_bwd_ref
 
 __all__ = ["attention_head", "attention_ref", "attention_ref_rows",
            "attention_ref_sp", "default_scale", "head_scores", "kv_head",
-           "softmax_rows"]
+           "softmax_rows", "attention_bwd_head", "attention_bwd_ref"]
