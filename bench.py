@@ -140,6 +140,8 @@ def main():
     ap.add_argument("--split", type=int, default=0,
                     help="time the split-KV entry point (attn_fwd_split) with this many key "
                          "ranges instead of attn_fwd (bf16 only)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time attn_bwd (gradients of the same forward; bf16 only)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the library-GEMM / zero-input context measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -222,6 +224,27 @@ def main():
                         "speedup_fused": round(m_ev / ev_mean, 2)}
         del s, p
 
+    backward = None
+    if args.backward and w.dtype == "bf16":
+        g = torch.Generator().manual_seed(w.seed + 9)
+        dout = torch.randn(qd.shape, generator=g).to(torch.bfloat16).cuda()
+        o_f, lse_f = attn.fwd(qd, kd, vd, scale)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws_b = torch.empty(attn.attn_bwd_workspace_bytes(w.B, w.Hq, w.N), dtype=torch.uint8,
+                           device="cuda")
+
+        def bstep():
+            attn.attn_bwd(qd, kd, vd, o_f, lse_f, dout, dq, dk, dv, ws_b, scale, stream)
+
+        with torch.cuda.stream(stream):
+            _, b_ms, _, _ = time_launches(bstep, stream, max(5, args.steps // 2), 3)
+        # the usual accounting: 5 N x N x d products = 2.5x the forward's FLOPs
+        # (the kernels run 7: S and dP are recomputed in both passes)
+        backward = {"ms": round(b_ms, 4), "tflops": round(2.5 * flops / (b_ms * 1e-3) / 1e12, 2),
+                    "flops": "2.5 x forward (5 products)", "executed_flops": "3.5 x forward",
+                    "fwd_plus_bwd_ms": round(b_ms + ev_mean, 4)}
+        del dout, o_f, lse_f, dq, dk, dv, ws_b
+
     ceiling = None
     if not args.no_ceiling and w.dtype == "bf16":
         qz, kz, vz = torch.zeros_like(qd), torch.zeros_like(kd), torch.zeros_like(vd)
@@ -246,6 +269,7 @@ def main():
         "pct_peak": round(100 * value / peak, 2),
         "roofline": roofline,
         "materialized": materialized,
+        "backward": backward,
         "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "kernel_source_sha": kernel_source_hash(),

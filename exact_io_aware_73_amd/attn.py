@@ -12,10 +12,12 @@ Entry points carry the C names and take tensors instead of raw pointers:
     attn_fwd_materialized_f32(q, k, v, o, lse, s, p, scale, stream=None)
     attn_fwd_split(q, k, v, o, lse, workspace, n_split, scale, stream=None)   bf16
     attn_fwd_split_workspace_bytes(B, Hq, N, d, n_split)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, stream=None)   bf16
+    attn_bwd_workspace_bytes(B, Hq, N)
     attn_strerror(status)
 
-plus ``fwd`` / ``fwd_materialized`` / ``fwd_split``, which allocate the outputs
-(and the split path's workspace) and pick the
+plus ``fwd`` / ``fwd_materialized`` / ``fwd_split`` / ``bwd``, which allocate
+the outputs (and the workspaces) and pick the
 entry point by dtype.  q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous
 CUDA (HIP) tensors.  Argument errors raise ValueError, launch errors
 RuntimeError.
@@ -49,6 +51,10 @@ _lib.attn_fwd_split.argtypes = [_P, _P, _P, _P, _P, _P, _U64, _I, _I, _I, _I, _I
 _lib.attn_fwd_split.restype = _I
 _lib.attn_fwd_split_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.attn_fwd_split_workspace_bytes.restype = _U64
+_lib.attn_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _U64, _I, _I, _I, _I, _I, _F, _P]
+_lib.attn_bwd.restype = _I
+_lib.attn_bwd_workspace_bytes.argtypes = [_I, _I, _I]
+_lib.attn_bwd_workspace_bytes.restype = _U64
 _lib.attn_strerror.argtypes = [_I]
 _lib.attn_strerror.restype = ctypes.c_char_p
 
@@ -171,6 +177,36 @@ def attn_fwd_split(q, k, v, o, lse, workspace, n_split, scale, stream=None):
     _raise(st, fn_name)
 
 
+def attn_bwd_workspace_bytes(B, Hq, N) -> int:
+    """Workspace bytes attn_bwd needs (0 for arguments it would reject)."""
+    return int(_lib.attn_bwd_workspace_bytes(int(B), int(Hq), int(N)))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, stream=None):
+    """Gradients of attn_fwd, bf16 I/O (C: attn_bwd)."""
+    fn_name = "attn_bwd"
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    for name, t, dt, shape in (("q", q, torch.bfloat16, q.shape), ("o", o, torch.bfloat16, q.shape),
+                               ("dout", dout, torch.bfloat16, q.shape),
+                               ("dq", dq, torch.bfloat16, q.shape), ("dk", dk, torch.bfloat16, k.shape),
+                               ("dv", dv, torch.bfloat16, k.shape), ("k", k, torch.bfloat16, k.shape),
+                               ("v", v, torch.bfloat16, k.shape), ("lse", lse, torch.float32, (B, Hq, N))):
+        if t.dtype != dt:
+            raise ValueError(f"{fn_name}: {name} must be {dt}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{fn_name}: {name} must be {tuple(shape)}, got {tuple(t.shape)}")
+        if t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{fn_name}: {name} must be contiguous on {q.device}")
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError(f"{fn_name}: workspace must be contiguous on {q.device}")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = _lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, Hq, Hkv, N, d,
+                           ctypes.c_float(float(scale)), _stream_handle(stream, q.device))
+    _raise(st, fn_name)
+
+
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
@@ -218,3 +254,14 @@ def fwd_split(q, k, v, n_split, scale=None, stream=None):
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     attn_fwd_split(q, k, v, o, lse, ws, n_split, _scale(scale, d), stream)
     return o, lse
+
+
+def bwd(q, k, v, o, lse, dout, scale=None, stream=None):
+    """(dq, dk, dv) of the forward (o, lse) = fwd(q, k, v, scale); bf16."""
+    B, Hq, _, N, d = _dims(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError(f"the backward takes bfloat16, got {q.dtype}")
+    ws = torch.empty(attn_bwd_workspace_bytes(B, Hq, N), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, _scale(scale, d), stream)
+    return dq, dk, dv

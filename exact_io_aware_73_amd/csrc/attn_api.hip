@@ -167,6 +167,45 @@ int split_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   return to_status(attn::launch_split_merge_bf16(a));
 }
 
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, void* ws, uint64_t ws_bytes, int B,
+             int Hq, int Hkv, int N, int d, float scale, void* stream) {
+  // the forward-shaped arguments first (q, k, v, o, lse as attn_fwd checks them)
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (!dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return ATTN_ERR_ALIGN;
+  const uint64_t rows = (uint64_t)B * Hq * N;
+  if (attn::bwd_grid(B, Hq, N) > kMaxWorkgroups || rows * 8 / 256 + 1 > kMaxWorkgroups)
+    return ATTN_ERR_SHAPE;
+  const uint64_t need = rows * 4;
+  if (!ws || !aligned(ws, 16) || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+  auto rng = [](const void* ptr, uint64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+    return Range{lo, lo + (uintptr_t)bytes};
+  };
+  const uint64_t qo = rows * d * 2, kv = (uint64_t)B * Hkv * N * d * 2;
+  const Range in[6] = {rng(q, qo), rng(k, kv), rng(v, kv), rng(o, qo), rng(lse, rows * 4),
+                       rng(dout, qo)};
+  const Range out[4] = {rng(dq, qo), rng(dk, kv), rng(dv, kv), rng(ws, need)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out[j])) return ATTN_ERR_ALIAS;
+  }
+  attn::FwdArgs a = make_args(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), nullptr,
+                              nullptr, B, Hq, Hkv, N, d, scale, stream);
+  attn::BwdArgs g;
+  g.dout = dout;
+  g.dq = dq;
+  g.dk = dk;
+  g.dv = dv;
+  g.dvec = static_cast<float*>(ws);
+  return to_status(attn::launch_bwd_bf16(a, g));
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,6 +265,23 @@ ATTN_API unsigned long long attn_fwd_split_workspace_bytes(int B, int Hq, int N,
       n_split > ATTN_MAX_SPLIT)
     return 0;
   return split_ws_bytes(B, Hq, N, d, n_split);
+}
+
+ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, unsigned long long workspace_bytes, int B, int Hq,
+                      int Hkv, int N, int d, float scale, void* stream) {
+  try {
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N,
+                    d, scale, stream);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+ATTN_API unsigned long long attn_bwd_workspace_bytes(int B, int Hq, int N) {
+  if (B < 1 || Hq < 1 || N < 1) return 0;
+  return (uint64_t)B * Hq * (uint64_t)N * 4u;
 }
 
 ATTN_API const char* attn_strerror(int status) {

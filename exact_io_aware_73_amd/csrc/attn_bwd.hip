@@ -1,0 +1,496 @@
+// attn_bwd.hip -- attention backward for gfx950: dQ, dK, dV from Q, K, V, O,
+// dO and the forward's lse, bf16 I/O, fp32 accumulation.
+//
+// The pages' backward (blog "attention 的显存线性化", section 五; the
+// "efficient attention" chapter's online-softmax section): the [N, N]
+// matrices of the forward are not kept; each block of S and P is recomputed
+// from Q, K and the saved per-row statistics when it is needed.  With the
+// forward's lse, P = exp(scale * Q K^T - lse) exactly, with no running max.
+// For the loss gradient dO = dL/dO the gradients of O = P V, P = softmax(S)
+// are (the chain rule through a row softmax):
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),  D_i = sum_c dO_ic O_ic,
+//   dQ = scale * dS K,   dK = scale * dS^T Q
+// (D_i = sum_j P_ij dP_ij, the row sum the softmax Jacobian subtracts).
+//
+// Three kernels:
+//   attn_bwd_rowdot  -- D_i per query row (fp32, into the caller's workspace);
+//   attn_bwd_dkdv    -- one workgroup per 128 keys of a K/V head: its K and V
+//                       rows stay in registers while the Q / dO tiles of every
+//                       query head of the group stream through LDS; dK and dV
+//                       accumulate in registers and are written once;
+//   attn_bwd_dq      -- one workgroup per 128 query rows: the K / V tiles of
+//                       the head stream through LDS (as in the forward) and dQ
+//                       accumulates in registers; no atomics anywhere.
+// S and dP are computed twice (once per kernel): 7 products per (query, key)
+// block instead of 5, traded for no atomic adds and no [N, N] storage.
+//
+// Layouts (v_mfma_f32_32x32x16_bf16; see mfma32x32x16 for operand slots):
+//  * dkdv: S = Q K^T and dP = dO V^T with the wave's K / V rows as the B
+//    operand (lane = key), so a lane holds 16 queries of one key; P and dS
+//    packed to bf16 are then directly the B operand of dV^T = dO^T P and
+//    dK^T = Q^T dS, whose A operands (dO^T, Q^T) come from transposing LDS
+//    reads of the row-major tiles.
+//  * dq: S^T = K Q^T and dP^T = V dO^T with the wave's Q / dO rows as the B
+//    operand (lane = query: lse and D are per-lane scalars); dS^T packed is
+//    the B operand of dQ^T = K^T dS^T, K^T read transposed from LDS.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kBWaves = 4;
+constexpr int kBThreads = kBWaves * kWave;
+constexpr int kWRows = 32;                    // rows a wave owns (keys in dkdv, queries in dq)
+constexpr int kWgRows = kBWaves * kWRows;     // rows a workgroup owns
+constexpr int kTRows = 64;                    // rows of a streamed LDS tile
+constexpr float kLog2e = 1.44269504088896341f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+template <int D>
+struct BGeo {
+  static constexpr int kKSteps = D / 16;               // MFMA k-steps over d
+  static constexpr int kDB = D / 32;                   // 32-wide d blocks
+  static constexpr int kCPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int kTile = kTRows * D;             // bf16 elements of one tile
+  static constexpr int kDma = kTile / 8 / kBThreads;   // 16-byte loads per lane per tile
+  static_assert(kDma * 8 * kBThreads == kTile, "tile must split over the workgroup");
+};
+
+// Chunk c of row r of a tile sits at chunk c ^ swz(r): both the 16-byte row
+// reads (MFMA A operands) and the transposing 8-byte reads are free of LDS
+// bank conflicts (the forward kernels' layout).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 128 ? (((row & 3) << 1) | ((row >> 2) & 1) | (row & 8))
+                  : ((((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1));
+}
+
+__device__ __forceinline__ int srows(int rem, int hi) {
+  int r;
+  asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2" : "=&s"(r) : "s"(rem), "s"(hi) : "scc");
+  return r;
+}
+
+// Rows j0 .. j0 + 63 of a [N, D] bf16 array -> the LDS tile at byte address
+// lds_tile, global -> LDS directly.  The buffer covers only rows j0 .. N-1:
+// rows past N read as zeros and nothing is read out of bounds.  Inline
+// assembly, as in the forward: the waits below order it against readers.
+template <int D>
+__device__ __forceinline__ void dma_tile(const __bf16* __restrict__ base, int j0, int N,
+                                         uint32_t lds_tile, int wave, const int* dvoff) {
+  using G = BGeo<D>;
+  const int rows = srows(N - j0, kTRows);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(base) + (int64_t)min(j0, N) * D, (short)0, rows * D * 2, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < G::kDma; ++i) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        lds_tile + (uint32_t)((wave * G::kDma + i) * kWave * 16));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 ::"s"(dst), "v"(dvoff[i]), "s"(rs) : "memory");
+  }
+}
+
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Per-lane LDS byte offsets of one tile's operand reads.
+template <int D>
+struct TileOffsets {
+  int dvoff[BGeo<D>::kDma];     // this lane's 16-byte chunks of a tile load
+  int row[BGeo<D>::kKSteps];    // 16-byte row read: row l32, chunk 2 s + hh
+  int tr[BGeo<D>::kDB];         // transposing read, rows +0..3 of a 16-row step
+  int tr8[BGeo<D>::kDB];        // the same, rows +8..11
+};
+
+template <int D>
+__device__ __forceinline__ TileOffsets<D> tile_offsets(int lane, int wave) {
+  using G = BGeo<D>;
+  TileOffsets<D> t;
+  const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < G::kDma; ++i) {
+    const int g = (wave * G::kDma + i) * kWave + lane;
+    const int row = g / G::kCPR;
+    t.dvoff[i] = (row * D + (((g % G::kCPR) ^ swz<D>(row)) * 8)) * 2;
+  }
+#pragma unroll
+  for (int s = 0; s < G::kKSteps; ++s) t.row[s] = (l32 * D + (((2 * s + hh) ^ swz<D>(l32)) * 8)) * 2;
+  // transposing read: in each 16-lane group, lane i points at row (i / 4)
+  // of a 4-row run and columns 4 (i % 4) .. +3 of the group's 16 columns;
+  // it receives rows 0..3 of column (group base + i)
+  const int li = lane & 15, dhalf = (lane >> 4) & 1;
+  const int vrow = 4 * hh + (li >> 2);
+#pragma unroll
+  for (int db = 0; db < G::kDB; ++db) {
+    const int dcol = db * 32 + dhalf * 16 + 4 * (li & 3);
+    t.tr[db] = (vrow * D + (((dcol >> 3) ^ swz<D>(vrow)) * 8) + (dcol & 7)) * 2;
+    t.tr8[db] = ((vrow + 8) * D + (((dcol >> 3) ^ swz<D>(vrow + 8)) * 8) + (dcol & 7)) * 2;
+  }
+  return t;
+}
+
+// A operand, rows r0 + l32 of the tile at byte address tile, k-step s.
+__device__ __forceinline__ bf16x8 lds_row(uint32_t tile, int off) {
+  const u32x4 u = *(const lds_u32x4*)(uintptr_t)(tile + off);
+  return as_bf16x8(u);
+}
+
+// A operand of a transposed product: columns = tile rows (16-row k-step at
+// byte offset rbase), rows = d block db.  Slot (hh, j) holds tile row
+// 8 (j / 4) + 4 hh + j % 4 of the step, matching the accumulator layout the
+// B operand comes from.
+__device__ __forceinline__ bf16x8 lds_tr(uint32_t tile, int off, int off8) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(tile + off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(tile + off8));
+  const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, a8);
+}
+
+// B operand from global memory: d = 16 s + 8 hh .. +7 of row `row` (rows
+// past N read row N - 1; their results are never used).
+template <int D>
+__device__ __forceinline__ void load_rowfrags(bf16x8 (&f)[BGeo<D>::kKSteps],
+                                              const __bf16* __restrict__ base, int row, int N,
+                                              int hh) {
+  const __bf16* p = base + (int64_t)min(row, N - 1) * D + 8 * hh;
+#pragma unroll
+  for (int s = 0; s < BGeo<D>::kKSteps; ++s) f[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(p + 16 * s));
+}
+
+// Store the transposed accumulator of a wave (rows = d, column = this
+// lane's row `row`), times `mul`, as bf16 row `row` of out.
+template <int D>
+__device__ __forceinline__ void store_rowT(const f32x16 (&acc)[BGeo<D>::kDB], __bf16* __restrict__ out,
+                                           float mul, int hh) {
+#pragma unroll
+  for (int db = 0; db < BGeo<D>::kDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[db][4 * r + 0] * mul, acc[db][4 * r + 1] * mul);
+      w[1] = pack_bf16x2(acc[db][4 * r + 2] * mul, acc[db][4 * r + 3] * mul);
+      *reinterpret_cast<u32x2*>(out + db * 32 + 8 * r + 4 * hh) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dO[i, c] * O[i, c]: eight lanes per row, fp32.
+template <int D>
+__global__ __launch_bounds__(256)
+void attn_bwd_rowdot_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
+                            float* __restrict__ dvec, int64_t n_rows) {
+  constexpr int kPer = D / 8;   // elements per lane
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t >> 3;
+  const int sub = (int)(t & 7);
+  float acc = 0.0f;
+  if (row < n_rows) {
+    const __bf16* po = o + row * D + sub * kPer;
+    const __bf16* pd = dout + row * D + sub * kPer;
+#pragma unroll
+    for (int c = 0; c < kPer; c += 8) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(po + c);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(pd + c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = __builtin_fmaf(bf16_bits_to_float(a[w] & 0xFFFFu), bf16_bits_to_float(b[w] & 0xFFFFu), acc);
+        acc = __builtin_fmaf(bf16_bits_to_float(a[w] >> 16), bf16_bits_to_float(b[w] >> 16), acc);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (row < n_rows && sub == 0) dvec[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per 128 keys of K/V head (b, kvh).
+template <int D>
+__global__ __launch_bounds__(kBThreads, D == 64 ? 2 : 1)
+void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                          const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                          const float* __restrict__ lse, const float* __restrict__ dvec,
+                          __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Hq, int Hkv,
+                          int N, float c_log2, float scale, int n_ktiles, uint32_t n_xcd) {
+  using G = BGeo<D>;
+  // per stage: Q tile, dO tile (bf16), then lse*log2e and D of its 64 rows
+  constexpr uint32_t kTileB = G::kTile * 2;
+  constexpr uint32_t kStageB = 2 * kTileB + 2 * kTRows * 4;
+  __shared__ __align__(16) unsigned char smem[2 * kStageB];
+  const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // key tiles fastest: the workgroups of one K/V head stream the same Q/dO
+  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
+  const int kt = (int)(logical % (uint32_t)n_ktiles);
+  const uint32_t rest = logical / (uint32_t)n_ktiles;
+  const int kvh = (int)(rest % (uint32_t)Hkv);
+  const int b = (int)(rest / (uint32_t)Hkv);
+  const int group = Hq / Hkv;
+  const int64_t head_kv = ((int64_t)b * Hkv + kvh) * (int64_t)N;
+
+  const int krow = kt * kWgRows + wave * kWRows + l32;   // this lane's key (B operand column)
+  bf16x8 kf[G::kKSteps], vf[G::kKSteps];
+  load_rowfrags<D>(kf, k + head_kv * D, krow, N, hh);
+  load_rowfrags<D>(vf, v + head_kv * D, krow, N, hh);
+
+  const TileOffsets<D> off = tile_offsets<D>(lane, wave);
+  f32x16 dkacc[G::kDB], dvacc[G::kDB];
+#pragma unroll
+  for (int i = 0; i < G::kDB; ++i) {
+    dkacc[i] = f32x16{};
+    dvacc[i] = f32x16{};
+  }
+
+  const int n_qt = (N + kTRows - 1) / kTRows;
+  const int n_steps = group * n_qt;   // (query head of the group, query tile)
+
+  // Loads of step t into stage t & 1: the Q and dO tiles go global -> LDS
+  // directly; lse*log2e and D of the 64 rows come through registers (rows
+  // past N get lse = +inf, so their weights are exp2(-inf) = 0, and D = 0).
+  float st_lse = 0.0f, st_d = 0.0f;
+  auto issue = [&](int t) {
+    const int h = kvh * group + t / n_qt;
+    const int q0 = (t % n_qt) * kTRows;
+    const int64_t head_q = ((int64_t)b * Hq + h) * (int64_t)N;
+    const uint32_t stage = lds + (uint32_t)(t & 1) * kStageB;
+    dma_tile<D>(q + head_q * D, q0, N, stage, wave, off.dvoff);
+    dma_tile<D>(dout + head_q * D, q0, N, stage + kTileB, wave, off.dvoff);
+    if (tid < kTRows) {
+      const int row = q0 + tid;
+      st_lse = row < N ? lse[head_q + row] * kLog2e : INFINITY;
+      st_d = row < N ? dvec[head_q + row] : 0.0f;
+    }
+  };
+  auto commit = [&](int t) {   // after the loads of step t have landed
+    if (tid < kTRows) {
+      const uint32_t stage = lds + (uint32_t)(t & 1) * kStageB;
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + tid * 4) = st_lse;
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + kTRows * 4 + tid * 4) = st_d;
+    }
+  };
+
+  issue(0);
+  wait_vm();
+  commit(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_steps; ++t) {
+    const uint32_t stage = lds + (uint32_t)(t & 1) * kStageB;
+    const uint32_t qtile = stage, dotile = stage + kTileB;
+    const uint32_t lse_s = stage + 2 * kTileB, d_s = lse_s + kTRows * 4;
+    if (t + 1 < n_steps) issue(t + 1);
+
+#pragma unroll
+    for (int qb = 0; qb < kTRows / 32; ++qb) {
+      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < G::kKSteps; ++s) {
+        const bf16x8 qa = lds_row(qtile + qb * 32 * D * 2, off.row[s]);
+        const bf16x8 da = lds_row(dotile + qb * 32 * D * 2, off.row[s]);
+        sacc = mfma32x32x16(qa, kf[s], sacc);
+        pacc = mfma32x32x16(da, vf[s], pacc);
+      }
+      // element 4 r + j: query qb*32 + 8 r + 4 hh + j
+      float p[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 l4 = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+        const f32x4 d4 = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * r + j;
+          p[e] = exp2_fast(__builtin_fmaf(sacc[e], c_log2, -l4[j]));
+          ds[e] = p[e] * (pacc[e] - d4[j]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 pu, du;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          pu[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
+          du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
+        }
+        const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
+#pragma unroll
+        for (int db = 0; db < G::kDB; ++db) {
+          dvacc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), dvacc[db]);
+          dkacc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dkacc[db]);
+        }
+      }
+    }
+    wait_vm();
+    if (t + 1 < n_steps) commit(t + 1);
+    __syncthreads();
+  }
+
+  if (krow < N) {
+    store_rowT<D>(dkacc, dk + (head_kv + krow) * D, scale, hh);
+    store_rowT<D>(dvacc, dv + (head_kv + krow) * D, 1.0f, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per 128 query rows of head (b, h).
+template <int D>
+__global__ __launch_bounds__(kBThreads, 2)
+void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                        const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                        const float* __restrict__ lse, const float* __restrict__ dvec,
+                        __bf16* __restrict__ dq, int Hq, int Hkv, int N, float c_log2, float scale,
+                        int n_qtiles, uint32_t n_xcd) {
+  using G = BGeo<D>;
+  constexpr uint32_t kTileB = G::kTile * 2;
+  constexpr uint32_t kStageB = 2 * kTileB;          // K tile, V tile
+  __shared__ __align__(16) unsigned char smem[2 * kStageB];
+  const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // query heads of a K/V group fastest, then query tiles (as the forward)
+  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
+  const int group = Hq / Hkv;
+  const int hg = (int)(logical % (uint32_t)group);
+  uint32_t rest = logical / (uint32_t)group;
+  const int qt = (int)(rest % (uint32_t)n_qtiles);
+  rest /= (uint32_t)n_qtiles;
+  const int kvh = (int)(rest % (uint32_t)Hkv);
+  const int b = (int)(rest / (uint32_t)Hkv);
+  const int h = kvh * group + hg;
+  const int64_t head_q = ((int64_t)b * Hq + h) * (int64_t)N;
+  const int64_t head_kv = ((int64_t)b * Hkv + kvh) * (int64_t)N;
+  const __bf16* kh = k + head_kv * D;
+  const __bf16* vh = v + head_kv * D;
+
+  const TileOffsets<D> off = tile_offsets<D>(lane, wave);
+  dma_tile<D>(kh, 0, N, lds, wave, off.dvoff);
+  dma_tile<D>(vh, 0, N, lds + kTileB, wave, off.dvoff);
+
+  const int qrow = qt * kWgRows + wave * kWRows + l32;   // this lane's query
+  const bool qvalid = qrow < N;
+  bf16x8 qf[G::kKSteps], df[G::kKSteps];
+  load_rowfrags<D>(qf, q + head_q * D, qrow, N, hh);
+  load_rowfrags<D>(df, dout + head_q * D, qrow, N, hh);
+  const int qr = min(qrow, N - 1);
+  const float lse2 = lse[head_q + qr] * kLog2e;
+  const float dd = dvec[head_q + qr];
+
+  f32x16 dqacc[G::kDB];
+#pragma unroll
+  for (int i = 0; i < G::kDB; ++i) dqacc[i] = f32x16{};
+
+  wait_vm();
+  __syncthreads();
+
+  const int n_kt = (N + kTRows - 1) / kTRows;
+  for (int jt = 0; jt < n_kt; ++jt) {
+    const uint32_t stage = lds + (uint32_t)(jt & 1) * kStageB;
+    const uint32_t ktile = stage, vtile = stage + kTileB;
+    if (jt + 1 < n_kt) {
+      const uint32_t nxt = lds + (uint32_t)((jt + 1) & 1) * kStageB;
+      dma_tile<D>(kh, (jt + 1) * kTRows, N, nxt, wave, off.dvoff);
+      dma_tile<D>(vh, (jt + 1) * kTRows, N, nxt + kTileB, wave, off.dvoff);
+    }
+    const int j0 = jt * kTRows;
+    const bool tail = j0 + kTRows > N;
+#pragma unroll
+    for (int kb = 0; kb < kTRows / 32; ++kb) {
+      // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < G::kKSteps; ++s) {
+        const bf16x8 ka = lds_row(ktile + kb * 32 * D * 2, off.row[s]);
+        const bf16x8 va = lds_row(vtile + kb * 32 * D * 2, off.row[s]);
+        sacc = mfma32x32x16(ka, qf[s], sacc);
+        pacc = mfma32x32x16(va, df[s], pacc);
+      }
+      // element e: key j0 + kb*32 + 8 (e / 4) + 4 hh + e % 4
+      float ds[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float pe = exp2_fast(__builtin_fmaf(sacc[e], c_log2, -lse2));
+        if (tail && j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3) >= N) pe = 0.0f;
+        ds[e] = pe * (pacc[e] - dd);
+      }
+      // dQ^T += K^T dS^T over the two 16-key k-steps
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 du;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
+        const uint32_t rb = (uint32_t)((kb * 32 + 16 * s2) * D * 2);
+#pragma unroll
+        for (int db = 0; db < G::kDB; ++db)
+          dqacc[db] = mfma32x32x16(lds_tr(ktile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dqacc[db]);
+      }
+    }
+    wait_vm();
+    __syncthreads();
+  }
+
+  if (qvalid) store_rowT<D>(dqacc, dq + (head_q + qrow) * D, scale, hh);
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, const BwdArgs& g) {
+  const float c_log2 = a.scale * kLog2e;
+  const int64_t n_rows = (int64_t)a.B * a.Hq * a.N;
+  const uint64_t grid0 = ((uint64_t)n_rows * 8 + 255) / 256;
+  hipLaunchKernelGGL((attn_bwd_rowdot_kernel<D>), dim3((uint32_t)grid0), dim3(256), 0, a.stream,
+                     static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(g.dout), g.dvec,
+                     n_rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_kt = (a.N + kWgRows - 1) / kWgRows;
+  const uint64_t grid1 = (uint64_t)n_kt * a.Hkv * a.B;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((uint32_t)grid1), dim3(kBThreads), 0, a.stream,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(g.dout), a.lse,
+                     g.dvec, static_cast<__bf16*>(g.dk), static_cast<__bf16*>(g.dv), a.Hq, a.Hkv,
+                     a.N, c_log2, a.scale, n_kt, (uint32_t)a.n_xcd);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_qt = (a.N + kWgRows - 1) / kWgRows;
+  const uint64_t grid2 = (uint64_t)n_qt * a.Hq * a.B;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((uint32_t)grid2), dim3(kBThreads), 0, a.stream,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(g.dout), a.lse,
+                     g.dvec, static_cast<__bf16*>(g.dq), a.Hq, a.Hkv, a.N, c_log2, a.scale, n_qt,
+                     (uint32_t)a.n_xcd);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+uint64_t bwd_grid(int B, int Hq, int N) {
+  return (uint64_t)((N + kWgRows - 1) / kWgRows) * Hq * B;
+}
+
+hipError_t launch_bwd_bf16(const FwdArgs& a, const BwdArgs& g) {
+  return a.d == 128 ? launch_d<128>(a, g) : launch_d<64>(a, g);
+}
+
+}  // namespace attn

@@ -43,6 +43,18 @@ hipError_t launch_fwd_bf16_rows64(const FwdArgs& a);
 inline bool fwd_bf16_use_rows64(int d) { return d == 128; }
 hipError_t launch_fwd_f32(const FwdArgs& a);
 
+// Backward (bf16): D = rowsum(dO * O) into dvec (fp32, B*Hq*N), then dK/dV
+// and dQ, recomputing S and P from q, k and lse.  a.o is the forward's O.
+struct BwdArgs {
+  const void* dout;   // dL/dO, like q
+  void* dq;           // like q
+  void* dk;           // like k
+  void* dv;           // like v
+  float* dvec;        // workspace: B*Hq*N floats
+};
+uint64_t bwd_grid(int B, int Hq, int N);
+hipError_t launch_bwd_bf16(const FwdArgs& a, const BwdArgs& g);
+
 // Split-KV forward (bf16): the rows64 kernel over key ranges of
 // split_chunk_keys(N, n_split) keys into part_o / part_lse, then the merge
 // of the ranges into o / lse.  The number of non-empty ranges is

@@ -155,6 +155,30 @@ ATTN_API int attn_fwd_split(const void* q, const void* k, const void* v, void* o
 ATTN_API unsigned long long attn_fwd_split_workspace_bytes(int B, int Hq, int N, int d,
                                                            int n_split);
 
+/*
+ * attn_bwd -- gradients of attn_fwd (bfloat16 I/O, float32 accumulation):
+ * given q, k, v, the forward's o and lse, and dout = dL/dO, writes
+ *   dq = dL/dQ, dk = dL/dK, dv = dL/dV
+ * (a K/V head's gradient sums over the query heads that share it).  The
+ * [N, N] matrices are recomputed block by block from q, k and lse, never
+ * stored (blog "attention 的显存线性化", section 五; "efficient attention"
+ * chapter, online-softmax section: recomputation in the backward pass).
+ *
+ * q, o, dout, dq: [B, Hq, N, d] bf16; k, v, dk, dv: [B, Hkv, N, d] bf16;
+ * lse: [B, Hq, N] float32 from attn_fwd with the same inputs and scale.
+ * workspace: a DEVICE buffer owned by the caller, 16-byte aligned, of at
+ * least attn_bwd_workspace_bytes(B, Hq, N) bytes (the row sums of dO * O);
+ * contents on entry do not matter.  Outputs and workspace must not overlap
+ * the inputs or each other.  Deterministic (no atomic accumulation).
+ */
+ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, unsigned long long workspace_bytes,
+                      int B, int Hq, int Hkv, int N, int d, float scale, void* stream);
+
+/* attn_bwd_workspace_bytes -- B * Hq * N * 4; 0 for B, Hq or N < 1. */
+ATTN_API unsigned long long attn_bwd_workspace_bytes(int B, int Hq, int N);
+
 /* attn_strerror -- a static, NUL-terminated description of a status code. */
 ATTN_API const char* attn_strerror(int status);
 

@@ -35,6 +35,9 @@ def lib():
     l.attn_fwd_split.argtypes = [P, P, P, P, P, P, ctypes.c_ulonglong, I, I, I, I, I, I, F, P]
     l.attn_fwd_split_workspace_bytes.argtypes = [I, I, I, I, I]
     l.attn_fwd_split_workspace_bytes.restype = ctypes.c_ulonglong
+    l.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_ulonglong, I, I, I, I, I, F, P]
+    l.attn_bwd_workspace_bytes.argtypes = [I, I, I]
+    l.attn_bwd_workspace_bytes.restype = ctypes.c_ulonglong
     l.attn_strerror.argtypes = [I]
     l.attn_strerror.restype = ctypes.c_char_p
     return l
@@ -43,7 +46,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert set(_declared()) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_materialized",
                                 "attn_fwd_materialized_f32", "attn_fwd_split",
-                                "attn_fwd_split_workspace_bytes", "attn_strerror"}
+                                "attn_fwd_split_workspace_bytes", "attn_bwd",
+                                "attn_bwd_workspace_bytes", "attn_strerror"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -153,3 +157,35 @@ def test_split_workspace_bytes_rejects(lib, args):
 ])
 def test_split_rejects(lib, kw, code):
     assert _split(lib, **kw) == _status_codes()[code]
+
+
+# ---------------------------------------------------------------------------
+# backward entry point
+DO_, DQ_, DK_, DV_, WB = (A * (i + 10) for i in range(5))
+
+
+def _bwd(lib, q=Q, k=K, v=V, o=O, lse=L, do=DO_, dq=DQ_, dk=DK_, dv=DV_, ws=WB, ws_bytes=1 << 40,
+         B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125):
+    return lib.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, N, d,
+                        ctypes.c_float(scale), None)
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.attn_bwd_workspace_bytes(2, 8, 1000) == 2 * 8 * 1000 * 4
+    assert lib.attn_bwd_workspace_bytes(0, 8, 1000) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, 0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), "ATTN_ERR_NULL"), (dict(dq=None), "ATTN_ERR_NULL"), (dict(dk=None), "ATTN_ERR_NULL"),
+    (dict(dv=None), "ATTN_ERR_NULL"), (dict(o=None), "ATTN_ERR_NULL"), (dict(lse=None), "ATTN_ERR_NULL"),
+    (dict(ws=None), "ATTN_ERR_WORKSPACE"), (dict(ws=WB + 4), "ATTN_ERR_WORKSPACE"),
+    (dict(ws_bytes=2 * 16 * 4 - 1), "ATTN_ERR_WORKSPACE"),
+    (dict(do=DO_ + 8), "ATTN_ERR_ALIGN"), (dict(dk=DK_ + 2), "ATTN_ERR_ALIGN"),
+    (dict(dq=Q), "ATTN_ERR_ALIAS"), (dict(dk=V + 32), "ATTN_ERR_ALIAS"), (dict(dv=DO_), "ATTN_ERR_ALIAS"),
+    (dict(dv=DK_ + 64), "ATTN_ERR_ALIAS"), (dict(ws=DQ_), "ATTN_ERR_ALIAS"), (dict(dq=L), "ATTN_ERR_ALIAS"),
+    (dict(Hq=3, Hkv=2), "ATTN_ERR_GQA"), (dict(d=32), "ATTN_ERR_HEADDIM"), (dict(N=0), "ATTN_ERR_SHAPE"),
+    (dict(scale=math.inf), "ATTN_ERR_SCALE"),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert _bwd(lib, **kw) == _status_codes()[code]

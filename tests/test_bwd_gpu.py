@@ -1,0 +1,98 @@
+"""GPU parity of the backward (attn_bwd, through the C ABI) against the fp64
+oracle (oracle/backward.py), on the same seeded bf16 inputs.
+
+Tolerance: the kernels round P and dS to bf16 (relative error 2^-9) before
+the products that consume them and the gradients to bf16 on output, and
+take D = rowsum(dO * O) from the forward's bf16 O; with fp32 accumulation
+the error of each gradient stays near a few 2^-9 of its largest entry.  The
+test allows 1 % of that entry (plus 1e-4 absolute, for gradients that are
+exactly zero in the reference).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def attn():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from exact_io_aware_73_amd import attn as a
+    return a
+
+
+def _grads(attn, q, k, v, do, scale):
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = attn.fwd(qd, kd, vd, scale)
+    dq, dk, dv = attn.bwd(qd, kd, vd, o, lse, dod, scale)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _check(attn, q, k, v, do, scale, label):
+    got = _grads(attn, q, k, v, do, scale)
+    ref = oracle.attention_bwd_ref(workloads.to_f64(q), workloads.to_f64(k), workloads.to_f64(v),
+                                   workloads.to_f64(do), scale)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        err = float(np.max(np.abs(workloads.to_f64(g) - r)))
+        tol = 1e-2 * float(np.max(np.abs(r))) + 1e-4
+        assert err <= tol, (label, name, err, tol)
+
+
+def _inputs(B, Hq, Hkv, N, d, seed):
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=seed)
+    do, _, _ = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=seed + 7)
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 127, 128, 129, 300])
+@pytest.mark.parametrize("B,Hq,Hkv", [(1, 1, 1), (2, 4, 2)])
+def test_bwd_small(attn, B, Hq, Hkv, N, d):
+    q, k, v, do = _inputs(B, Hq, Hkv, N, d, 31 * N + d + Hq)
+    _check(attn, q, k, v, do, 1 / math.sqrt(d), f"bwd {B},{Hq},{Hkv},{N},{d}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, 0.4])
+def test_bwd_scales(attn, scale):
+    q, k, v, do = _inputs(1, 2, 1, 200, 64, 77)
+    _check(attn, q, k, v, do, scale, f"scale {scale}")
+
+
+def test_bwd_longer_gqa(attn):
+    q, k, v, do = _inputs(1, 4, 1, 1024, 128, 91)
+    _check(attn, q, k, v, do, 1 / math.sqrt(128), "N=1024 GQA 4:1")
+
+
+def test_bwd_deterministic(attn):
+    q, k, v, do = _inputs(2, 8, 2, 700, 128, 5)
+    a = _grads(attn, q, k, v, do, 0.09)
+    b = _grads(attn, q, k, v, do, 0.09)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_single_key(attn):
+    """N = 1: dV = dO (summed over the group), dQ = dK = 0 up to rounding."""
+    q, k, v, do = _inputs(2, 4, 2, 1, 64, 3)
+    dq, dk, dv = _grads(attn, q, k, v, do, 0.3)
+    assert dq.abs().max().item() <= 1e-4 and dk.abs().max().item() <= 1e-4
+    want = workloads.to_f64(do).reshape(2, 2, 2, 1, 64).sum(axis=2)
+    assert np.max(np.abs(workloads.to_f64(dv) - want)) <= 2 ** -7 * np.max(np.abs(want))
+
+
+def test_python_bwd_rejects(attn):
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = attn.fwd(q, q, q)
+    ws = torch.empty(4, dtype=torch.uint8, device="cuda")   # too small
+    with pytest.raises(ValueError):
+        attn.attn_bwd(q, q, q, o, lse, q, torch.empty_like(q), torch.empty_like(q),
+                      torch.empty_like(q), ws, 0.125)
+    with pytest.raises(ValueError):
+        attn.bwd(q.float(), q.float(), q.float(), o, lse, q)
