@@ -297,44 +297,97 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     const uint32_t lse_s = stage + 2 * kTileB, d_s = lse_s + kTRows * 4;
     if (t + 1 < n_steps) issue(t + 1);
 
+    if constexpr (D == 128) {
+      // d = 128 (one wave per SIMD: the wave itself has to keep the matrix
+      // core busy): S = Q K^T and dP = dO V^T for both 32-query blocks first,
+      // so the products of block 1 overlap the weights of block 0 (7 % faster)
+      constexpr int kQB = kTRows / 32;
+      f32x16 sacc[kQB], pacc[kQB];
 #pragma unroll
-    for (int qb = 0; qb < kTRows / 32; ++qb) {
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      for (int qb = 0; qb < kQB; ++qb) {
+        sacc[qb] = f32x16{};
+        pacc[qb] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < G::kKSteps; ++s) {
-        const bf16x8 qa = lds_row(qtile + qb * 32 * D * 2, off.row[s]);
-        const bf16x8 da = lds_row(dotile + qb * 32 * D * 2, off.row[s]);
-        sacc = mfma32x32x16(qa, kf[s], sacc);
-        pacc = mfma32x32x16(da, vf[s], pacc);
-      }
-      // element 4 r + j: query qb*32 + 8 r + 4 hh + j
-      float p[16], ds[16];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f32x4 l4 = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
-        const f32x4 d4 = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * r + j;
-          p[e] = exp2_fast(__builtin_fmaf(sacc[e], c_log2, -l4[j]));
-          ds[e] = p[e] * (pacc[e] - d4[j]);
+        for (int s = 0; s < G::kKSteps; ++s) {
+          const bf16x8 qa = lds_row(qtile + qb * 32 * D * 2, off.row[s]);
+          const bf16x8 da = lds_row(dotile + qb * 32 * D * 2, off.row[s]);
+          sacc[qb] = mfma32x32x16(qa, kf[s], sacc[qb]);
+          pacc[qb] = mfma32x32x16(da, vf[s], pacc[qb]);
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 pu, du;
+      for (int qb = 0; qb < kQB; ++qb) {
+        // element 4 r + j: query qb*32 + 8 r + 4 hh + j
+        float p[16], ds[16];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pu[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
-          du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 l4 = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+          const f32x4 d4 = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * r + j;
+            p[e] = exp2_fast(__builtin_fmaf(sacc[qb][e], c_log2, -l4[j]));
+            ds[e] = p[e] * (pacc[qb][e] - d4[j]);
+          }
         }
-        const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
+        // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
 #pragma unroll
-        for (int db = 0; db < G::kDB; ++db) {
-          dvacc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), dvacc[db]);
-          dkacc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dkacc[db]);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 pu, du;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pu[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
+            du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
+          }
+          const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
+#pragma unroll
+          for (int db = 0; db < G::kDB; ++db) {
+            dvacc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), dvacc[db]);
+            dkacc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dkacc[db]);
+          }
+        }
+      }
+    } else {
+      // d = 64 (two waves per SIMD): block by block, the other wave fills in
+#pragma unroll
+      for (int qb = 0; qb < kTRows / 32; ++qb) {
+        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < G::kKSteps; ++s) {
+          const bf16x8 qa = lds_row(qtile + qb * 32 * D * 2, off.row[s]);
+          const bf16x8 da = lds_row(dotile + qb * 32 * D * 2, off.row[s]);
+          sacc = mfma32x32x16(qa, kf[s], sacc);
+          pacc = mfma32x32x16(da, vf[s], pacc);
+        }
+        // element 4 r + j: query qb*32 + 8 r + 4 hh + j
+        float p[16], ds[16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 l4 = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+          const f32x4 d4 = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * r + j;
+            p[e] = exp2_fast(__builtin_fmaf(sacc[e], c_log2, -l4[j]));
+            ds[e] = p[e] * (pacc[e] - d4[j]);
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 pu, du;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pu[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
+            du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
+          }
+          const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
+#pragma unroll
+          for (int db = 0; db < G::kDB; ++db) {
+            dvacc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), dvacc[db]);
+            dkacc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dkacc[db]);
+          }
         }
       }
     }
