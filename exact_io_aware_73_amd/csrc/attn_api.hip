@@ -94,8 +94,8 @@ int fwd_impl(bool bf16, const void* q, const void* k, const void* v, void* o, fl
   if (st != ATTN_OK) return st;
   const bool rows64 = attn::fwd_bf16_use_rows64(d);
   const uint64_t grid = !bf16 ? attn::fwd_f32_grid(B, Hq, N)
-                      : rows64 ? attn::fwd_bf16_rows64_grid(B, Hq, N)
-                               : attn::fwd_bf16_rows32_grid(B, Hq, N);
+                      : rows64 ? attn::fwd_bf16_rows64_grid(B, Hq, Hkv, N)
+                               : attn::fwd_bf16_rows32_grid(B, Hq, Hkv, N);
   if (grid > kMaxWorkgroups) return ATTN_ERR_SHAPE;
   const int elem = bf16 ? 2 : 4;
   st = check_alias(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, elem, 0);
@@ -139,7 +139,7 @@ int split_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   const uint64_t chunk = attn::split_chunk_keys(N, n_split);
   const int n_eff = (int)(((uint64_t)N + chunk - 1) / chunk);   // non-empty ranges
   const uint64_t rows = (uint64_t)B * Hq * N;
-  if (attn::fwd_bf16_rows64_grid(B, Hq, N) * n_eff > kMaxWorkgroups ||
+  if (attn::fwd_bf16_rows64_grid(B, Hq, Hkv, N) * n_eff > kMaxWorkgroups ||
       rows * (uint64_t)(d / 8) / 256 + 1 > kMaxWorkgroups)
     return ATTN_ERR_SHAPE;
   const uint64_t need = split_ws_bytes(B, Hq, N, d, n_split);
@@ -177,7 +177,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return ATTN_ERR_ALIGN;
   const uint64_t rows = (uint64_t)B * Hq * N;
-  if (attn::bwd_grid(B, Hq, N) > kMaxWorkgroups || rows * 8 / 256 + 1 > kMaxWorkgroups)
+  if (attn::bwd_grid(B, Hq, Hkv, N) > kMaxWorkgroups || rows * 8 / 256 + 1 > kMaxWorkgroups)
     return ATTN_ERR_SHAPE;
   const uint64_t need = rows * 4;
   if (!ws || !aligned(ws, 16) || ws_bytes < need) return ATTN_ERR_WORKSPACE;

@@ -242,8 +242,11 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   const uint32_t rest = logical / (uint32_t)n_ktiles;
   const int kvh = (int)(rest % (uint32_t)Hkv);
   const int b = (int)(rest / (uint32_t)Hkv);
-  const int group = Hq / Hkv;
   const int64_t head_kv = ((int64_t)b * Hkv + kvh) * (int64_t)N;
+  // the query heads of the group are adjacent in q, dO, lse and D: their
+  // rows form one block of (Hq / Hkv) * N rows, streamed 64 at a time
+  const int n_qrows = (Hq / Hkv) * N;
+  const int64_t head_q = ((int64_t)b * Hkv + kvh) * (int64_t)n_qrows;
 
   const int krow = kt * kWgRows + wave * kWRows + l32;   // this lane's key (B operand column)
   bf16x8 kf[G::kKSteps], vf[G::kKSteps];
@@ -258,24 +261,22 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     dvacc[i] = f32x16{};
   }
 
-  const int n_qt = (N + kTRows - 1) / kTRows;
-  const int n_steps = group * n_qt;   // (query head of the group, query tile)
+  const int n_steps = (n_qrows + kTRows - 1) / kTRows;   // 64-row query tiles of the group
 
   // Loads of step t into stage t & 1: the Q and dO tiles go global -> LDS
   // directly; lse*log2e and D of the 64 rows come through registers (rows
-  // past N get lse = +inf, so their weights are exp2(-inf) = 0, and D = 0).
+  // past the group's last get lse = +inf, so their weights are
+  // exp2(-inf) = 0, and D = 0).
   float st_lse = 0.0f, st_d = 0.0f;
   auto issue = [&](int t) {
-    const int h = kvh * group + t / n_qt;
-    const int q0 = (t % n_qt) * kTRows;
-    const int64_t head_q = ((int64_t)b * Hq + h) * (int64_t)N;
+    const int q0 = t * kTRows;
     const uint32_t stage = lds + (uint32_t)(t & 1) * kStageB;
-    dma_tile<D>(q + head_q * D, q0, N, stage, wave, off.dvoff);
-    dma_tile<D>(dout + head_q * D, q0, N, stage + kTileB, wave, off.dvoff);
+    dma_tile<D>(q + head_q * D, q0, n_qrows, stage, wave, off.dvoff);
+    dma_tile<D>(dout + head_q * D, q0, n_qrows, stage + kTileB, wave, off.dvoff);
     if (tid < kTRows) {
       const int row = q0 + tid;
-      st_lse = row < N ? lse[head_q + row] * kLog2e : INFINITY;
-      st_d = row < N ? dvec[head_q + row] : 0.0f;
+      st_lse = row < n_qrows ? lse[head_q + row] * kLog2e : INFINITY;
+      st_d = row < n_qrows ? dvec[head_q + row] : 0.0f;
     }
   };
   auto commit = [&](int t) {   // after the loads of step t have landed
@@ -423,17 +424,15 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // query heads of a K/V group fastest, then query tiles (as the forward)
+  // query tiles over the group's (Hq / Hkv) * N adjacent rows, numbered
+  // fastest (as the forward)
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
-  const int group = Hq / Hkv;
-  const int hg = (int)(logical % (uint32_t)group);
-  uint32_t rest = logical / (uint32_t)group;
-  const int qt = (int)(rest % (uint32_t)n_qtiles);
-  rest /= (uint32_t)n_qtiles;
+  const int qt = (int)(logical % (uint32_t)n_qtiles);
+  const uint32_t rest = logical / (uint32_t)n_qtiles;
   const int kvh = (int)(rest % (uint32_t)Hkv);
   const int b = (int)(rest / (uint32_t)Hkv);
-  const int h = kvh * group + hg;
-  const int64_t head_q = ((int64_t)b * Hq + h) * (int64_t)N;
+  const int n_qrows = (Hq / Hkv) * N;
+  const int64_t head_q = ((int64_t)b * Hkv + kvh) * (int64_t)n_qrows;
   const int64_t head_kv = ((int64_t)b * Hkv + kvh) * (int64_t)N;
   const __bf16* kh = k + head_kv * D;
   const __bf16* vh = v + head_kv * D;
@@ -443,11 +442,11 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
   dma_tile<D>(vh, 0, N, lds + kTileB, wave, off.dvoff);
 
   const int qrow = qt * kWgRows + wave * kWRows + l32;   // this lane's query
-  const bool qvalid = qrow < N;
+  const bool qvalid = qrow < n_qrows;
   bf16x8 qf[G::kKSteps], df[G::kKSteps];
-  load_rowfrags<D>(qf, q + head_q * D, qrow, N, hh);
-  load_rowfrags<D>(df, dout + head_q * D, qrow, N, hh);
-  const int qr = min(qrow, N - 1);
+  load_rowfrags<D>(qf, q + head_q * D, qrow, n_qrows, hh);
+  load_rowfrags<D>(df, dout + head_q * D, qrow, n_qrows, hh);
+  const int qr = min(qrow, n_qrows - 1);
   const float lse2 = lse[head_q + qr] * kLog2e;
   const float dd = dvec[head_q + qr];
 
@@ -526,8 +525,8 @@ hipError_t launch_d(const FwdArgs& a, const BwdArgs& g) {
                      a.N, c_log2, a.scale, n_kt, (uint32_t)a.n_xcd);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_qt = (a.N + kWgRows - 1) / kWgRows;
-  const uint64_t grid2 = (uint64_t)n_qt * a.Hq * a.B;
+  const int n_qt = (int)(((uint64_t)(a.Hq / a.Hkv) * a.N + kWgRows - 1) / kWgRows);
+  const uint64_t grid2 = (uint64_t)n_qt * a.Hkv * a.B;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((uint32_t)grid2), dim3(kBThreads), 0, a.stream,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(g.dout), a.lse,
@@ -538,8 +537,8 @@ hipError_t launch_d(const FwdArgs& a, const BwdArgs& g) {
 
 }  // namespace
 
-uint64_t bwd_grid(int B, int Hq, int N) {
-  return (uint64_t)((N + kWgRows - 1) / kWgRows) * Hq * B;
+uint64_t bwd_grid(int B, int Hq, int Hkv, int N) {
+  return ((uint64_t)(Hq / Hkv) * N + kWgRows - 1) / kWgRows * Hkv * B;
 }
 
 hipError_t launch_bwd_bf16(const FwdArgs& a, const BwdArgs& g) {

@@ -168,21 +168,22 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
     dvoff[i] = (row * D + c * 8) * 2;
   }
 
-  // ---- which (b, head, query tile) this workgroup owns -------------------
+  // ---- which (b, K/V head, query tile) this workgroup owns ----------------
+  // The query heads that share a K/V head are adjacent in q, o and lse, so
+  // the rows of a group form one block of (Hq / Hkv) * N rows; query tiles
+  // run over that block (a tile may end in one head and go on in the next),
+  // so one K/V stream serves every head of the group and heads shorter than
+  // a tile leave no rows idle.  Query tiles are numbered fastest: workgroups
+  // that stream the same K/V rows at the same time run side by side on one
+  // XCD and share its L2.
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
-  // the query heads that share a K/V head are numbered fastest, then query
-  // tiles: workgroups that stream the same K/V rows at the same time run
-  // side by side on one XCD and share its L2
-  const int group = Hq / Hkv;
-  const int hg = (int)(logical % (uint32_t)group);
-  uint32_t rest = logical / (uint32_t)group;
-  const int qt = (int)(rest % (uint32_t)n_qtiles);
-  rest /= (uint32_t)n_qtiles;
+  const int qt = (int)(logical % (uint32_t)n_qtiles);
+  const uint32_t rest = logical / (uint32_t)n_qtiles;
   const int kvh = (int)(rest % (uint32_t)Hkv);
   const int b = (int)(rest / (uint32_t)Hkv);
-  const int h = kvh * group + hg;
 
-  const int64_t head_q = ((int64_t)b * Hq + h) * (int64_t)N;     // row index base
+  const int n_qrows = (Hq / Hkv) * N;                                // rows of the group
+  const int64_t head_q = ((int64_t)b * Hkv + kvh) * (int64_t)n_qrows; // its first row
   const int64_t head_kv = ((int64_t)b * Hkv + kvh) * (int64_t)N;
   const __bf16* kh = k + head_kv * D;
   const __bf16* vh = v + head_kv * D;
@@ -193,7 +194,7 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
   dma_tile<D>(vh, 0, N, lds + G::kTile * 2, wave, dvoff);
 
   const int qrow = qt * kFBr + wave * kFRows + l32;   // this lane's query
-  const bool qvalid = qrow < N;
+  const bool qvalid = qrow < n_qrows;
 
   // ---- Q^T fragments: lane holds d = 16 s + 8 hh .. +7 of its query -------
   bf16x8 qf[G::kKSteps];
@@ -373,8 +374,8 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
 
 template <int D, bool kNeg>
 hipError_t launch_d(const FwdArgs& a) {
-  const int n_qtiles = (a.N + kFBr - 1) / kFBr;
-  const uint64_t grid = (uint64_t)n_qtiles * a.Hq * a.B;
+  const int n_qtiles = (int)(((uint64_t)(a.Hq / a.Hkv) * a.N + kFBr - 1) / kFBr);
+  const uint64_t grid = (uint64_t)n_qtiles * a.Hkv * a.B;
   const float c_log2 = a.scale * 1.44269504088896341f;
   hipLaunchKernelGGL((attn_fwd_bf16_rows32_kernel<D, kNeg>), dim3((uint32_t)grid), dim3(kFThreads), 0,
                      a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
@@ -385,8 +386,8 @@ hipError_t launch_d(const FwdArgs& a) {
 
 }  // namespace
 
-uint64_t fwd_bf16_rows32_grid(int B, int Hq, int N) {
-  return (uint64_t)((N + kFBr - 1) / kFBr) * Hq * B;
+uint64_t fwd_bf16_rows32_grid(int B, int Hq, int Hkv, int N) {
+  return ((uint64_t)(Hq / Hkv) * N + kFBr - 1) / kFBr * Hkv * B;
 }
 
 hipError_t launch_fwd_bf16_rows32(const FwdArgs& a) {

@@ -9,8 +9,8 @@ namespace {
 
 template <int D, bool kNeg>
 hipError_t launch_d(const FwdArgs& a) {
-  const int n_qtiles = (a.N + kFBr - 1) / kFBr;
-  const uint64_t grid = (uint64_t)n_qtiles * a.Hq * a.B;
+  const int n_qtiles = (int)(((uint64_t)(a.Hq / a.Hkv) * a.N + kFBr - 1) / kFBr);
+  const uint64_t grid = (uint64_t)n_qtiles * a.Hkv * a.B;
   const float c_log2 = a.scale * 1.44269504088896341f;
   hipLaunchKernelGGL((attn_fwd_bf16_rows64_kernel<D, kNeg>), dim3((uint32_t)grid), dim3(kFThreads), 0,
                      a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
@@ -21,8 +21,8 @@ hipError_t launch_d(const FwdArgs& a) {
 
 }  // namespace
 
-uint64_t fwd_bf16_rows64_grid(int B, int Hq, int N) {
-  return (uint64_t)((N + kFBr - 1) / kFBr) * Hq * B;
+uint64_t fwd_bf16_rows64_grid(int B, int Hq, int Hkv, int N) {
+  return ((uint64_t)(Hq / Hkv) * N + kFBr - 1) / kFBr * Hkv * B;
 }
 
 hipError_t launch_fwd_bf16_rows64(const FwdArgs& a) {

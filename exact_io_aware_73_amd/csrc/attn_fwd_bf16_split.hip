@@ -10,8 +10,8 @@ namespace {
 
 template <int D, bool kNeg>
 hipError_t launch_split_d(const FwdArgs& a) {
-  const int n_qtiles = (a.N + kFBr - 1) / kFBr;
-  const uint64_t grid = (uint64_t)n_qtiles * a.Hq * a.B * a.n_split;
+  const int n_qtiles = (int)(((uint64_t)(a.Hq / a.Hkv) * a.N + kFBr - 1) / kFBr);
+  const uint64_t grid = (uint64_t)n_qtiles * a.Hkv * a.B * a.n_split;
   const float c_log2 = a.scale * 1.44269504088896341f;
   hipLaunchKernelGGL((attn_fwd_bf16_rows64_split_kernel<D, kNeg>), dim3((uint32_t)grid),
                      dim3(kFThreads), 0, a.stream, static_cast<const __bf16*>(a.q),

@@ -28,8 +28,8 @@ struct FwdArgs {
 };
 
 // workgroup counts (for the launch-size check)
-uint64_t fwd_bf16_rows32_grid(int B, int Hq, int N);
-uint64_t fwd_bf16_rows64_grid(int B, int Hq, int N);
+uint64_t fwd_bf16_rows32_grid(int B, int Hq, int Hkv, int N);
+uint64_t fwd_bf16_rows64_grid(int B, int Hq, int Hkv, int N);
 uint64_t fwd_f32_grid(int B, int Hq, int N);
 
 // Fused bf16 forward, two kernel designs:
@@ -52,7 +52,7 @@ struct BwdArgs {
   void* dv;           // like v
   float* dvec;        // workspace: B*Hq*N floats
 };
-uint64_t bwd_grid(int B, int Hq, int N);
+uint64_t bwd_grid(int B, int Hq, int Hkv, int N);
 hipError_t launch_bwd_bf16(const FwdArgs& a, const BwdArgs& g);
 
 // Split-KV forward (bf16): the rows64 kernel over key ranges of

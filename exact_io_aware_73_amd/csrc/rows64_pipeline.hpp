@@ -500,16 +500,17 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- which (b, head, query tile) this workgroup owns -------------------
+  // ---- which (b, K/V head, query tile) this workgroup owns ----------------
+  // The query heads that share a K/V head are adjacent in q, o and lse, so
+  // the rows of a group form one block of (Hq / Hkv) * N rows; query tiles
+  // run over that block (a tile may end in one head and go on in the next),
+  // so one K/V stream serves every head of the group and heads shorter than
+  // a tile leave no rows idle.  Query tiles are numbered fastest: workgroups
+  // that stream the same K/V rows at the same time run side by side on one
+  // XCD and share its L2.
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
-  // the query heads that share a K/V head are numbered fastest, then query
-  // tiles: workgroups that stream the same K/V rows at the same time run
-  // side by side on one XCD and share its L2
-  const int group = Hq / Hkv;
-  const int hg = (int)(logical % (uint32_t)group);
-  uint32_t rest = logical / (uint32_t)group;
-  const int qt = (int)(rest % (uint32_t)n_qtiles);
-  rest /= (uint32_t)n_qtiles;
+  const int qt = (int)(logical % (uint32_t)n_qtiles);
+  uint32_t rest = logical / (uint32_t)n_qtiles;
 #if ATTN_ROWS64_SPLIT
   // the key range next: all query tiles of one range run side by side
   const int split = (int)(rest % (uint32_t)n_split);
@@ -517,9 +518,9 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
 #endif
   const int kvh = (int)(rest % (uint32_t)Hkv);
   const int b = (int)(rest / (uint32_t)Hkv);
-  const int h = kvh * group + hg;
 
-  const int64_t head_q = ((int64_t)b * Hq + h) * (int64_t)N;     // row index base
+  const int n_qrows = (Hq / Hkv) * N;                                // rows of the group
+  const int64_t head_q = ((int64_t)b * Hkv + kvh) * (int64_t)n_qrows; // its first row
   const int64_t head_kv = ((int64_t)b * Hkv + kvh) * (int64_t)N;
 #if ATTN_ROWS64_SPLIT
   // this workgroup's keys: the range [k0, k0 + Nk) of its split
@@ -538,7 +539,7 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int qrow = qt * kFBr + wave * kFRows + qb * 32 + l32;
-    const bool qvalid = qrow < N;
+    const bool qvalid = qrow < n_qrows;
     const __bf16* qp = q + (head_q + (qvalid ? qrow : 0)) * D + 8 * hh;
 #pragma unroll
     for (int st = 0; st < G::kKSteps; ++st) {
@@ -626,7 +627,7 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
     const int qrow = qt * kFBr + wave * kFRows + qb * 32 + l32;
     const float l_tot = xhalf_sum(w.l[qb]);
 #if ATTN_ROWS64_SPLIT
-    if (qrow < N) {
+    if (qrow < n_qrows) {
       // partial result of this key range: O / l in fp32 and its lse
       const float inv = 1.0f / l_tot;
       const int64_t prow = (int64_t)split * n_rows + head_q + qrow;
@@ -643,7 +644,7 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
       if (hh == 0) part_lse[prow] = (w.m[qb] + log2_fast(l_tot)) * 0.69314718055994531f;
     }
 #else
-    if (qrow < N) {
+    if (qrow < n_qrows) {
       const float inv = 1.0f / l_tot;
       __bf16* orow = o + (head_q + qrow) * D;
 #pragma unroll

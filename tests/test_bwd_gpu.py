@@ -59,6 +59,14 @@ def test_bwd_small(attn, B, Hq, Hkv, N, d):
     _check(attn, q, k, v, do, 1 / math.sqrt(d), f"bwd {B},{Hq},{Hkv},{N},{d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 16, 1, 1), (1, 16, 1, 33), (2, 12, 3, 100), (1, 32, 4, 77)])
+def test_bwd_gqa_packed(attn, B, Hq, Hkv, N, d):
+    """Query tiles shared by the heads of a K/V group, crossing head boundaries."""
+    q, k, v, do = _inputs(B, Hq, Hkv, N, d, 37 * N + d + Hq)
+    _check(attn, q, k, v, do, 1 / math.sqrt(d), f"bwd packed {B},{Hq},{Hkv},{N},{d}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.1, 0.4])
 def test_bwd_scales(attn, scale):
     q, k, v, do = _inputs(1, 2, 1, 200, 64, 77)

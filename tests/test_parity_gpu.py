@@ -71,6 +71,31 @@ def test_fused_f32_small(attn, B, Hq, Hkv, N, d):
     _check_full(attn, q, k, v, 1.0 / math.sqrt(d), torch.float32, "fused f32")
 
 
+# The query heads of a K/V group are packed into shared query tiles: tiles
+# that cross head boundaries, groups of more rows than a tile, one row per head.
+PACKED = [(1, 16, 1, 1), (1, 16, 1, 33), (2, 12, 3, 100), (1, 32, 4, 77), (1, 8, 8, 45), (1, 4, 2, 300)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,Hq,Hkv,N", PACKED)
+def test_fused_bf16_gqa_packed(attn, B, Hq, Hkv, N, d):
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=19 * N + d + Hq)
+    _check_full(attn, q, k, v, 1.0 / math.sqrt(d), torch.bfloat16, "packed GQA bf16")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N", PACKED[1:4])
+def test_split_gqa_packed(attn, B, Hq, Hkv, N):
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, 128, torch.bfloat16, seed=23 * N + Hq)
+    scale = 1.0 / math.sqrt(128)
+    _say(f"[parity] split packed q={tuple(q.shape)} k={tuple(k.shape)}")
+    o, lse = attn.fwd_split(q.cuda(), k.cuda(), v.cuda(), 3, scale)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = oracle.attention_ref(workloads.to_f64(q), workloads.to_f64(k),
+                                          workloads.to_f64(v), scale)
+    r = compare(workloads.to_f64(o.cpu()), lse.cpu().numpy(), O_ref, lse_ref, "bf16")
+    assert r["ok"], r
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [512, 500])
 def test_many_workgroups(attn, N, d):

@@ -67,6 +67,9 @@ WORKLOADS = {
         Workload("one_head_b1_h1_n32768_d128", 1, 1, 1, 32768, 128, "bf16", 6000,
                  description="one long head: 128 query tiles of 256 rows for 256 compute "
                              "units, the case the split-KV path is for"),
+        Workload("gqa_short_b64_hq32_hkv4_n200_d128", 64, 32, 4, 200, 128, "bf16", 7000,
+                 description="grouped-query attention on short sequences, 8 query heads "
+                             "per K/V head: heads shorter than a query tile"),
     ]
 }
 
