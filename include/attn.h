@@ -39,8 +39,9 @@
  * aborts or lets an exception escape.  attn_strerror() names a code.
  *
  * Sizes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128}.  Element
- * offsets are computed in 64 bits; B*Hq*ceil(N/128) workgroups must fit the
- * launch grid (< 2^31 / 256 workgroups).
+ * offsets are computed in 64 bits; B*Hkv*ceil((Hq/Hkv)*N/128) workgroups
+ * (the query tiles run over the adjacent rows of the heads that share a
+ * K/V head) must fit the launch grid (< 2^31 / 256 workgroups).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
