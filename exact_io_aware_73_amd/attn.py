@@ -55,6 +55,8 @@ _lib.attn_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _U64, _I, _I, 
 _lib.attn_bwd.restype = _I
 _lib.attn_bwd_workspace_bytes.argtypes = [_I, _I, _I]
 _lib.attn_bwd_workspace_bytes.restype = _U64
+_lib.attn_fwd_fp8.argtypes = [_P, _P, _P, _P, _P, _F, _F, _F, _I, _I, _I, _I, _I, _F, _P]
+_lib.attn_fwd_fp8.restype = _I
 _lib.attn_strerror.argtypes = [_I]
 _lib.attn_strerror.restype = ctypes.c_char_p
 
@@ -177,6 +179,44 @@ def attn_fwd_split(q, k, v, o, lse, workspace, n_split, scale, stream=None):
     _raise(st, fn_name)
 
 
+_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def fp8_padded_keys(N: int) -> int:
+    """Row length of the transposed V of attn_fwd_fp8: N rounded up to 16."""
+    return (int(N) + 15) // 16 * 16
+
+
+def attn_fwd_fp8(q8, k8, vt8, o, lse, q_scale, k_scale, v_scale, scale, stream=None):
+    """8-bit forward (C: attn_fwd_fp8).  q8 [B,Hq,N,d], k8 [B,Hkv,N,d] and
+    vt8 [B,Hkv,d,Np] (V transposed, Np = fp8_padded_keys(N)) hold OCP E4M3
+    codes (uint8 or float8_e4m3fn); o bf16 [B,Hq,N,d]; lse fp32 [B,Hq,N]."""
+    fn_name = "attn_fwd_fp8"
+    for name, t in (("q8", q8), ("k8", k8), ("vt8", vt8)):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{fn_name}: {name} must be a contiguous 4-D device tensor")
+        if t.dtype not in _FP8_DTYPES:
+            raise ValueError(f"{fn_name}: {name} must be uint8 or float8_e4m3fn, got {t.dtype}")
+    B, Hq, N, d = q8.shape
+    Hkv = k8.shape[1]
+    want = {"k8": (B, Hkv, N, d), "vt8": (B, Hkv, d, fp8_padded_keys(N)), "o": (B, Hq, N, d),
+            "lse": (B, Hq, N)}
+    for name, t, dt in (("k8", k8, None), ("vt8", vt8, None), ("o", o, torch.bfloat16),
+                        ("lse", lse, torch.float32)):
+        if tuple(t.shape) != want[name]:
+            raise ValueError(f"{fn_name}: {name} must be {want[name]}, got {tuple(t.shape)}")
+        if dt is not None and t.dtype != dt:
+            raise ValueError(f"{fn_name}: {name} must be {dt}, got {t.dtype}")
+        if t.device != q8.device or not t.is_contiguous():
+            raise ValueError(f"{fn_name}: {name} must be contiguous on {q8.device}")
+    with torch.cuda.device(q8.device):
+        st = _lib.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(o), _ptr(lse),
+                               ctypes.c_float(float(q_scale)), ctypes.c_float(float(k_scale)),
+                               ctypes.c_float(float(v_scale)), B, Hq, Hkv, N, d,
+                               ctypes.c_float(float(scale)), _stream_handle(stream, q8.device))
+    _raise(st, fn_name)
+
+
 def attn_bwd_workspace_bytes(B, Hq, N) -> int:
     """Workspace bytes attn_bwd needs (0 for arguments it would reject)."""
     return int(_lib.attn_bwd_workspace_bytes(int(B), int(Hq), int(N)))
@@ -265,3 +305,12 @@ def bwd(q, k, v, o, lse, dout, scale=None, stream=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, _scale(scale, d), stream)
     return dq, dk, dv
+
+
+def fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, scale=None, stream=None):
+    """(o, lse) of the 8-bit forward; o is bf16; scale defaults to 1/sqrt(d)."""
+    B, Hq, N, d = q8.shape
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    attn_fwd_fp8(q8, k8, vt8, o, lse, q_scale, k_scale, v_scale, _scale(scale, d), stream)
+    return o, lse

@@ -206,6 +206,35 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   return to_status(attn::launch_bwd_bf16(a, g));
 }
 
+int fp8_impl(const void* q8, const void* k8, const void* vt8, void* o, float* lse, float q_scale,
+             float k_scale, float v_scale, int B, int Hq, int Hkv, int N, int d, float scale,
+             void* stream) {
+  int st = check_common(q8, k8, vt8, o, lse, B, Hq, Hkv, N, d, scale);
+  if (st != ATTN_OK) return st;
+  const float c = scale * q_scale * k_scale;
+  if (!isfinite(q_scale) || !isfinite(k_scale) || !isfinite(v_scale) || !isfinite(c))
+    return ATTN_ERR_SCALE;
+  const uint64_t np = (uint64_t)attn::fp8_padded_keys(N);
+  // a head's V^T (d rows of Np bytes) is addressed with 32-bit offsets
+  if (np * (uint64_t)d >= (1ull << 31) || attn::fwd_fp8_grid(B, Hq, Hkv, N) > kMaxWorkgroups)
+    return ATTN_ERR_SHAPE;
+  auto rng = [](const void* ptr, uint64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+    return Range{lo, lo + (uintptr_t)bytes};
+  };
+  const uint64_t rows = (uint64_t)B * Hq * N;
+  const Range in[3] = {rng(q8, rows * d), rng(k8, (uint64_t)B * Hkv * N * d),
+                       rng(vt8, (uint64_t)B * Hkv * d * np)};
+  const Range out[2] = {rng(o, rows * d * 2), rng(lse, rows * 4)};
+  for (int i = 0; i < 2; ++i)
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return ATTN_ERR_ALIAS;
+  if (overlap(out[0], out[1])) return ATTN_ERR_ALIAS;
+  attn::FwdArgs a = make_args(q8, k8, vt8, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, c, stream);
+  a.v_scale = v_scale;
+  return to_status(attn::launch_fwd_fp8(a));
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,6 +272,17 @@ ATTN_API int attn_fwd_materialized_f32(const float* q, const float* k, const flo
                                        int N, int d, float scale, void* stream) {
   try {
     return materialized_impl(false, q, k, v, o, lse, s, p, B, Hq, Hkv, N, d, scale, stream);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+ATTN_API int attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, float* lse,
+                          float q_scale, float k_scale, float v_scale, int B, int Hq, int Hkv,
+                          int N, int d, float scale, void* stream) {
+  try {
+    return fp8_impl(q8, k8, vt8, o, lse, q_scale, k_scale, v_scale, B, Hq, Hkv, N, d, scale,
+                    stream);
   } catch (...) {
     return ATTN_ERR_HIP;
   }

@@ -24,6 +24,9 @@ struct FwdArgs {
   int chunk_keys = 0;
   float* part_o = nullptr;
   float* part_lse = nullptr;
+  // 8-bit path only: the V scale (q, k, v are E4M3 codes; v is V^T, [B,Hkv,d,Np];
+  // scale already holds scale * q_scale * k_scale)
+  float v_scale = 1.0f;
   hipStream_t stream;
 };
 
@@ -42,6 +45,11 @@ hipError_t launch_fwd_bf16_rows32(const FwdArgs& a);
 hipError_t launch_fwd_bf16_rows64(const FwdArgs& a);
 inline bool fwd_bf16_use_rows64(int d) { return d == 128; }
 hipError_t launch_fwd_f32(const FwdArgs& a);
+
+// 8-bit (OCP E4M3) forward on the FP8 MFMA; V^T rows of Np = fp8_padded_keys(N) bytes.
+int fp8_padded_keys(int N);
+uint64_t fwd_fp8_grid(int B, int Hq, int Hkv, int N);
+hipError_t launch_fwd_fp8(const FwdArgs& a);
 
 // Backward (bf16): D = rowsum(dO * O) into dvec (fp32, B*Hq*N), then dK/dV
 // and dQ, recomputing S and P from q, k and lse.  a.o is the forward's O.

@@ -123,6 +123,44 @@ ATTN_API int attn_fwd_materialized_f32(const float* q, const float* k, const flo
                                        void* stream);
 
 /*
+ * attn_fwd_fp8 -- the fused tiled forward with 8-bit floating-point inputs
+ * on the FP8 matrix cores (the pages list FP8 among the third FlashAttention
+ * version's features without its arithmetic: blog "attention 的显存线性化",
+ * section 五).
+ *
+ * q8  : [B, Hq,  N,  d]  OCP 8-bit floating point E4M3 codes (1 sign, 4
+ *                        exponent bits with bias 7, 3 mantissa bits; no
+ *                        infinities; 0x7F / 0xFF are NaN), one byte each
+ * k8  : [B, Hkv, N,  d]  E4M3
+ * vt8 : [B, Hkv, d, Np]  E4M3, V TRANSPOSED (key index fastest), rows padded
+ *                        to Np = N rounded up to a multiple of 16 keys; the
+ *                        padding bytes are ignored (they may hold anything)
+ * o   : [B, Hq,  N,  d]  bf16;   lse : [B, Hq, N] float32, natural log
+ * The values are q = q_scale * q8, k = k_scale * k8, v = v_scale * v8; the
+ * result is attention of those values with `scale` as in attn_fwd.
+ *
+ * Accuracy contract: the scores are the exact 8-bit products summed by
+ * the matrix core into fp32, within 2^-14 * |scale| * sum_c |q_c k_c| of
+ * exact; lse uses the unrounded weights, so its error is that of the
+ * scores.  The one lossy step: each softmax weight p = exp(S - m) -- m a
+ * running row maximum, at most 2 (log2 units) below the row's true maximum
+ * when the largest weights are met -- is scaled by 2^6 and rounded to E4M3
+ * before the PV product (relative error <= 2^-4; absolute error <= 2^-16
+ * of the row's largest weight); the exp-sum uses the unrounded weights.
+ * Hence per element |O - O_exact| <= sum_j (2^-4 w_j + 2^-16 max_k w_k)
+ * |v_jc|, plus the score error's effect, fp32 and the bf16 output
+ * rounding, with w the exact softmax weights.
+ *
+ * Pointers: q8, k8, vt8, o 16-byte aligned, lse 4-byte aligned; outputs
+ * must not overlap the inputs or each other.  q_scale, k_scale, v_scale and
+ * scale * q_scale * k_scale must be finite (ATTN_ERR_SCALE).  d in {64, 128};
+ * d * Np must be below 2^31.  Deterministic.
+ */
+ATTN_API int attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, float* lse,
+                          float q_scale, float k_scale, float v_scale, int B, int Hq, int Hkv,
+                          int N, int d, float scale, void* stream);
+
+/*
  * attn_fwd_split -- the fused forward with every head's keys cut into up to
  * n_split contiguous ranges of whole 32-key tiles, each range handled by its
  * own workgroups (for heads too few or too long to fill the GPU: one head of

@@ -35,10 +35,15 @@ The reading taken here, stated as the contract of the 8-bit entry point:
         sum_j (p~_j - p_j) v_j / sum_j p_j,
     so per output element (i, c)
         |O'_ic - O_ic| <= sum_j (u * w_ij + e * w_i,max) * |v_jc|,
-    e = 2^-16.  ``fp8_error_bound`` returns that, plus 2^-12 * sum_j w_ij |v_jc|
-    for the fp32 arithmetic around it (scores from exact 8-bit products
-    summed in fp32, exp2, the fp32 sums).  The final rounding of O to bf16
-    is the caller's to add.
+    e = 2^-16.  ``fp8_error_bound`` returns that, plus two slack terms on
+    the relative part: 2^-12 for the fp32 arithmetic (exp2, the sums), and
+    2 * eps_s * max_j A_ij for the scores, A_ij = |scale| * sum_c |q_ic| |k_jc|:
+    the matrix core sums the exact 8-bit products into fp32 with an error
+    the contract bounds by eps_s * A_ij, eps_s = 2^-14 (a score error
+    dS_j moves the normalised weight w_j by a factor within
+    exp(+-2 max_j |dS_j|)).  The same eps_s * max_j A_ij bounds the error of
+    lse (``fp8_lse_bound``).  The final rounding of O to bf16 is the
+    caller's to add.
   * For a statistical check: with independent rounding errors of relative
     size <= u (mean square <= u^2 / 3), the mean square of O' - O is at most
     (u^2 / 3) * sum_j w_ij^2 v_jc^2 per element; ``fp8_mean_square_bound``.
@@ -52,6 +57,7 @@ from .attention import attention_ref, head_scores, kv_head, softmax_rows
 U_E4M3 = 2.0 ** -4          # relative rounding error bound of E4M3 (3 mantissa bits)
 E_ABS = 2.0 ** -16          # absolute weight error bound, relative to the row's largest
 FP32_SLACK = 2.0 ** -12     # fp32 arithmetic around the 8-bit products
+EPS_S = 2.0 ** -14          # score error allowed per unit of sum_c |q_c k_c| * |scale|
 
 
 def padded_keys(N: int) -> int:
@@ -86,7 +92,9 @@ def attention_fp8_ref(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
     return attention_ref(q, k, v, scale)
 
 
-def _weights_and_v(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
+def _heads(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
+    """Per (b, h): exact weights W, the K/V head's v, and each row's
+    score-error bound eps_s * max_j |scale| sum_c |q_ic| |k_jc|."""
     N = np.asarray(q8).shape[2]
     q, k, v = dequantize(q8, k8, vt8, q_scale, k_scale, v_scale, N)
     B, Hq = q.shape[:2]
@@ -95,17 +103,28 @@ def _weights_and_v(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
         for h in range(Hq):
             kv = kv_head(h, Hq, Hkv)
             W, _ = softmax_rows(head_scores(q[b, h], k[b, kv], scale))
-            yield b, h, W, v[b, kv]
+            ds = EPS_S * abs(scale) * (np.abs(q[b, h]) @ np.abs(k[b, kv]).T).max(axis=1)
+            yield b, h, W, v[b, kv], ds
 
 
 def fp8_error_bound(q8, k8, vt8, q_scale, k_scale, v_scale, scale) -> np.ndarray:
     """Per-element bound on |O_path - O| (before the output's bf16 rounding)."""
     q8 = np.asarray(q8)
     out = np.zeros(q8.shape, dtype=np.float64)
-    for b, h, W, v in _weights_and_v(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
+    for b, h, W, v, ds in _heads(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
         av = np.abs(v)
-        out[b, h] = ((U_E4M3 + FP32_SLACK) * (W @ av)
+        rel = U_E4M3 + FP32_SLACK + 2.0 * ds[:, None]
+        out[b, h] = (rel * (W @ av)
                      + E_ABS * W.max(axis=1, keepdims=True) * av.sum(axis=0, keepdims=True))
+    return out
+
+
+def fp8_lse_bound(q8, k8, vt8, q_scale, k_scale, v_scale, scale) -> np.ndarray:
+    """Per-row bound on |lse_path - lse|: the score error bound of the row."""
+    q8 = np.asarray(q8)
+    out = np.zeros(q8.shape[:3], dtype=np.float64)
+    for b, h, _, _, ds in _heads(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
+        out[b, h] = ds
     return out
 
 
@@ -114,6 +133,6 @@ def fp8_mean_square_bound(q8, k8, vt8, q_scale, k_scale, v_scale, scale) -> np.n
     weight roundings: (u^2 / 3) * sum_j w_ij^2 v_jc^2."""
     q8 = np.asarray(q8)
     out = np.zeros(q8.shape, dtype=np.float64)
-    for b, h, W, v in _weights_and_v(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
+    for b, h, W, v, _ in _heads(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
         out[b, h] = (U_E4M3 ** 2 / 3.0) * ((W * W) @ (v * v))
     return out

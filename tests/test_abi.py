@@ -38,6 +38,7 @@ def lib():
     l.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_ulonglong, I, I, I, I, I, F, P]
     l.attn_bwd_workspace_bytes.argtypes = [I, I, I]
     l.attn_bwd_workspace_bytes.restype = ctypes.c_ulonglong
+    l.attn_fwd_fp8.argtypes = [P, P, P, P, P, F, F, F, I, I, I, I, I, F, P]
     l.attn_strerror.argtypes = [I]
     l.attn_strerror.restype = ctypes.c_char_p
     return l
@@ -47,7 +48,7 @@ def test_header_declares_the_entry_points():
     assert set(_declared()) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_materialized",
                                 "attn_fwd_materialized_f32", "attn_fwd_split",
                                 "attn_fwd_split_workspace_bytes", "attn_bwd",
-                                "attn_bwd_workspace_bytes", "attn_strerror"}
+                                "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_strerror"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -189,3 +190,31 @@ def test_bwd_workspace_bytes(lib):
 ])
 def test_bwd_rejects(lib, kw, code):
     assert _bwd(lib, **kw) == _status_codes()[code]
+
+
+# ---------------------------------------------------------------------------
+# 8-bit entry point (host-side checks only: every case is rejected before any
+# HIP call).  Inputs: q8 / k8 1 byte per element, vt8 [B, Hkv, d, Np].
+Q8, K8, VT8, O8, L8 = (A * (i + 20) for i in range(5))
+
+
+def _fp8(lib, q=Q8, k=K8, vt=VT8, o=O8, lse=L8, qs=0.5, ks=0.5, vs=0.25, B=1, Hq=2, Hkv=1, N=17,
+         d=128, scale=0.125):
+    return lib.attn_fwd_fp8(q, k, vt, o, lse, ctypes.c_float(qs), ctypes.c_float(ks),
+                            ctypes.c_float(vs), B, Hq, Hkv, N, d, ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), "ATTN_ERR_NULL"), (dict(vt=None), "ATTN_ERR_NULL"), (dict(lse=None), "ATTN_ERR_NULL"),
+    (dict(Hq=3, Hkv=2), "ATTN_ERR_GQA"), (dict(d=96), "ATTN_ERR_HEADDIM"), (dict(N=0), "ATTN_ERR_SHAPE"),
+    (dict(B=0), "ATTN_ERR_SHAPE"), (dict(scale=math.nan), "ATTN_ERR_SCALE"),
+    (dict(qs=math.inf), "ATTN_ERR_SCALE"), (dict(vs=math.nan), "ATTN_ERR_SCALE"),
+    (dict(qs=3e38, ks=3e38), "ATTN_ERR_SCALE"),        # the combined multiplier overflows
+    (dict(N=1 << 24), "ATTN_ERR_SHAPE"),               # d * Np reaches 2^31
+    (dict(vt=VT8 + 8), "ATTN_ERR_ALIGN"), (dict(o=O8 + 2), "ATTN_ERR_ALIGN"),
+    (dict(lse=L8 + 2), "ATTN_ERR_ALIGN"),
+    (dict(o=Q8), "ATTN_ERR_ALIAS"), (dict(o=VT8 + 128 * 32 - 16), "ATTN_ERR_ALIAS"),
+    (dict(lse=K8 + 16), "ATTN_ERR_ALIAS"), (dict(lse=O8 + 64), "ATTN_ERR_ALIAS"),
+])
+def test_fp8_rejects(lib, kw, code):
+    assert _fp8(lib, **kw) == _status_codes()[code]

@@ -169,13 +169,38 @@ def test_bound_fails_with_halved_u():
 
 
 def test_oracle_bound_matches_direct_form():
-    """fp8_error_bound on 8-bit inputs equals the direct formula on the decoded values."""
+    """fp8_error_bound on 8-bit inputs equals the direct formula on the decoded
+    values, with the score term 2 eps_s max_j |scale| sum_c |q_ic k_jc| added
+    to the relative part; fp8_lse_bound is that score term's half."""
     q8, k8, vt8 = _random_fp8(1, 2, 1, 50, 32, 9)
-    b = F.fp8_error_bound(q8, k8, vt8, 0.7, 1.1, 0.5, 0.2)
+    b = F.fp8_error_bound(q8, k8, vt8, 0.7, 1.1, 0.5, -0.2)
+    lb = F.fp8_lse_bound(q8, k8, vt8, 0.7, 1.1, 0.5, -0.2)
     q, k, v = F.dequantize(q8, k8, vt8, 0.7, 1.1, 0.5, 50)
     for h in range(2):
-        S = 0.2 * q[0, h] @ k[0, 0].T
-        np.testing.assert_allclose(b[0, h], _bound_from(S, v[0, 0]), rtol=1e-12)
+        S = -0.2 * q[0, h] @ k[0, 0].T
+        A = 0.2 * np.abs(q[0, h]) @ np.abs(k[0, 0]).T          # >= |S| entrywise
+        assert np.all(A >= np.abs(S) - 1e-12)
+        ds = F.EPS_S * A.max(axis=1)
+        W = oracle.softmax_rows(S)[0]
+        want = _bound_from(S, v[0, 0]) + 2.0 * ds[:, None] * (W @ np.abs(v[0, 0]))
+        np.testing.assert_allclose(b[0, h], want, rtol=1e-12)
+        np.testing.assert_allclose(lb[0, h], ds, rtol=1e-12)
+
+
+def test_score_perturbation_within_bound():
+    """Scores perturbed by up to eps_s * A_ij (the contract's score error) move O
+    by less than the score term of the bound."""
+    rng = np.random.default_rng(3)
+    q8, k8, vt8 = _random_fp8(1, 1, 1, 300, 64, 4)
+    q, k, v = F.dequantize(q8, k8, vt8, 1.0, 1.0, 1.0, 300)
+    S = 0.125 * q[0, 0] @ k[0, 0].T
+    A = 0.125 * np.abs(q[0, 0]) @ np.abs(k[0, 0]).T
+    dS = F.EPS_S * A * rng.choice([-1.0, 1.0], size=A.shape)
+    W0, l0 = oracle.softmax_rows(S)
+    W1, l1 = oracle.softmax_rows(S + dS)
+    ds = F.EPS_S * A.max(axis=1)
+    assert np.all(np.abs(l1 - l0) <= ds)
+    assert np.all(np.abs(W1 @ v[0, 0] - W0 @ v[0, 0]) <= 2.0 * ds[:, None] * (W0 @ np.abs(v[0, 0])) * 1.01)
 
 
 def test_mean_square_bound_holds_under_emulation():

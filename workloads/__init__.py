@@ -131,3 +131,53 @@ def random_inputs(B, Hq, Hkv, N, d, dtype: torch.dtype, seed: int, std: float = 
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a CPU/GPU tensor (bf16 or fp32) to a float64 NumPy array."""
     return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# 8-bit inputs (OCP E4M3 codes, one scale per tensor) for the FP8 entry point
+
+def _e4m3_codes(x: torch.Tensor) -> torch.Tensor:
+    """Round-to-nearest-even E4M3 codes of x (|x| must stay within 448) as uint8."""
+    return x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+
+def _pad_keys(vt: torch.Tensor, N: int) -> torch.Tensor:
+    """[.., d, N] -> [.., d, Np] with Np = N rounded up to 16 (zero codes)."""
+    Np = (N + 15) // 16 * 16
+    out = torch.zeros(vt.shape[:-1] + (Np,), dtype=vt.dtype)
+    out[..., :N] = vt
+    return out.contiguous()
+
+
+def fp8_inputs(B, Hq, Hkv, N, d, seed: int, kind: str = "normal"):
+    """Seeded 8-bit (q8, k8, vt8, q_scale, k_scale, v_scale) on the CPU.
+
+    kind "normal": i.i.d. N(0,1) values, each tensor scaled so its largest
+    magnitude maps to 224 and rounded to E4M3 (the decoded codes times the
+    scale are the inputs).  kind "exact": q and k rows with three entries of
+    +-1 at seeded positions (scale 1), so every score q.k is an integer in
+    [-3, 3]; v i.i.d. normal as above.
+    vt8 is V transposed, [B, Hkv, d, Np], its padding keys zero codes.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 17)
+    v = _randn((B, Hkv, N, d), seed + 2)
+    v_scale = float(v.abs().max()) / 224.0
+    vt8 = _pad_keys(_e4m3_codes((v / v_scale).transpose(-1, -2)), N)
+    if kind == "normal":
+        q = _randn((B, Hq, N, d), seed + 0)
+        k = _randn((B, Hkv, N, d), seed + 1)
+        q_scale = float(q.abs().max()) / 224.0
+        k_scale = float(k.abs().max()) / 224.0
+        return _e4m3_codes(q / q_scale), _e4m3_codes(k / k_scale), vt8, q_scale, k_scale, v_scale
+    if kind == "exact":
+        def sparse_pm1(shape):
+            x = torch.zeros(shape)
+            idx = torch.stack([torch.randperm(d, generator=g)[:3] for _ in range(x.numel() // d)])
+            sign = torch.randint(0, 2, idx.shape, generator=g).float() * 2.0 - 1.0
+            x.view(-1, d).scatter_(1, idx, sign)
+            return x
+        q = sparse_pm1((B, Hq, N, d))
+        k = sparse_pm1((B, Hkv, N, d))
+        return _e4m3_codes(q), _e4m3_codes(k), vt8, 1.0, 1.0, v_scale
+    raise ValueError(f"unknown kind {kind!r}")
