@@ -142,6 +142,9 @@ def main():
                          "ranges instead of attn_fwd (bf16 only)")
     ap.add_argument("--backward", action="store_true",
                     help="also time attn_bwd (gradients of the same forward; bf16 only)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the 8-bit entry point (attn_fwd_fp8) on the workload's shape: "
+                         "E4M3 codes of seeded N(0,1) values with per-tensor scales")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the library-GEMM / zero-input context measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -185,6 +188,17 @@ def main():
         def entry(q_, k_, v_, o_, lse_, scale_, stream_):
             attn.attn_fwd_split(q_, k_, v_, o_, lse_, ws, args.split, scale_, stream_)
 
+    fp8 = None
+    if args.fp8:
+        if w.dtype != "bf16" or args.split or args.backward:
+            sys.exit("--fp8 takes a bf16 workload's shape and runs the 8-bit forward alone")
+        fp8 = workloads.fp8_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed)
+        q8d, k8d, vt8d = (t.cuda() for t in fp8[:3])
+        q_s, k_s, v_s = fp8[3:]
+
+        def entry(q_, k_, v_, o_, lse_, scale_, stream_):
+            attn.attn_fwd_fp8(q8d, k8d, vt8d, o_, lse_, q_s, k_s, v_s, scale_, stream_)
+
     def step():
         entry(qd, kd, vd, o, lse, scale, stream)
 
@@ -194,10 +208,11 @@ def main():
     flops = acc.attn_fwd_flops(w.B, w.Hq, w.N, w.d)
     minb = acc.min_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.elem_bytes)
     value = flops / (ms_step * 1e-3) / 1e12
-    peak = acc.PEAK_BF16_TFLOPS if w.dtype == "bf16" else acc.PEAK_FP32_VECTOR_TFLOPS
+    peak = (acc.PEAK_FP8_TFLOPS if fp8 else
+            acc.PEAK_BF16_TFLOPS if w.dtype == "bf16" else acc.PEAK_FP32_VECTOR_TFLOPS)
     achieved = flops / (ev_mean * 1e-3) / 1e12
-    # the byte counters are taken on attn_fwd; the split path has its own kernels
-    traffic = None if args.split else traffic_from_profiles(w.name, flops)
+    # the byte counters are taken on attn_fwd; the split and 8-bit paths have their own kernels
+    traffic = None if (args.split or fp8) else traffic_from_profiles(w.name, flops)
     roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel_ms_mean": round(ev_mean, 4),
@@ -206,7 +221,8 @@ def main():
                 "traffic_vs_min": (round(traffic / minb, 3) if traffic else None)}
 
     materialized = None
-    if not args.no_materialized and w.B * w.Hq * w.N * w.N * (4 + w.elem_bytes) < (64 << 30):
+    if (not args.no_materialized and not fp8
+            and w.B * w.Hq * w.N * w.N * (4 + w.elem_bytes) < (64 << 30)):
         s = torch.empty((w.B, w.Hq, w.N, w.N), dtype=torch.float32, device="cuda")
         p = torch.empty((w.B, w.Hq, w.N, w.N), dtype=w.torch_dtype, device="cuda")
         o2 = torch.empty_like(qd)
@@ -246,7 +262,7 @@ def main():
         del dout, o_f, lse_f, dq, dk, dv, ws_b
 
     ceiling = None
-    if not args.no_ceiling and w.dtype == "bf16":
+    if not args.no_ceiling and w.dtype == "bf16" and not fp8:
         qz, kz, vz = torch.zeros_like(qd), torch.zeros_like(kd), torch.zeros_like(vd)
         ceiling = mfma_ceiling(lambda: entry(qz, kz, vz, o, lse, scale, stream), stream, flops,
                                args.steps)
@@ -255,16 +271,24 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        if fp8:
+            # the 8-bit oracle is the plain definition on the dequantised inputs
+            import oracle
+            q, k, v = (torch.from_numpy(x) for x in oracle.dequantize(
+                fp8[0].numpy(), fp8[1].numpy(), fp8[2].numpy(), *fp8[3:], w.N))
         cpu = cpu_baseline(w, q, k, v, scale, args.cpu_budget)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "dtype": "fp8_e4m3" if fp8 else ("bf16" if w.dtype == "bf16" else "f32"),
+        "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "io_dtype": w.dtype, "parallelism": "none", "inputs": "iid N(0,1), seeded",
+                   "io_dtype": "e4m3 in, bf16 out" if fp8 else w.dtype, "parallelism": "none",
+                   "inputs": "iid N(0,1), seeded" + (", E4M3 with per-tensor scales" if fp8 else ""),
                    "entry": f"attn_fwd_split(n_split={args.split})" if args.split else
+                            "attn_fwd_fp8" if fp8 else
                             ("attn_fwd" if w.dtype == "bf16" else "attn_fwd_f32")},
         "pct_peak": round(100 * value / peak, 2),
         "roofline": roofline,

@@ -77,6 +77,7 @@ XCD_COUNT = 8
 PEAK_CLOCK_GHZ = 2.4
 BF16_DENSE_FLOP_PER_CLK_PER_CU = 4096
 PEAK_BF16_TFLOPS = 2516.6          # 256 CU * 2.4 GHz * 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2           # dense FP8 MFMA: twice the bf16 rate
 PEAK_FP32_VECTOR_TFLOPS = 157.3    # packed fp32 FMA
 PEAK_HBM_GBPS = 8000.0
 
