@@ -30,10 +30,12 @@
 //    current one is computed.  Rows sit unpadded with their 16-byte chunks
 //    XOR-swizzled by the row index, so both the MFMA operand reads of K and
 //    the transposing reads of V are free of LDS bank conflicts.
-//  * The scale is folded into exp2: p = 2^(s * scale * log2 e - m).  The
-//    running max is only moved when some row's max grows by more than
-//    kRescaleLog2 (softmax is unchanged by any common shift of a row, the
-//    basis of the rescale rule), so the rescale of the accumulator is rare.
+//  * The scale is folded into exp2: p = 2^(s * scale * log2 e - m).  Since
+//    softmax is unchanged by any common shift of a row (the basis of the
+//    rescale rule), m need only keep the weights bounded: a full tile is
+//    weighted against m as it stands and kept if its exp-sum stays under a
+//    cap; only the first tile, the tail tile and a tile over the cap take
+//    the tile's row max, move m and rescale the accumulator.
 //  * Workgroups of one K/V head are numbered consecutively and remapped so
 //    they run on one XCD and share its L2.
 #include <hip/hip_runtime.h>
@@ -50,7 +52,7 @@ constexpr int kFWaves = 4;
 constexpr int kFThreads = kFWaves * kWave;
 constexpr int kFRows = 32;                   // query rows per wave
 constexpr int kFBr = kFWaves * kFRows;       // query rows per workgroup
-constexpr float kRescaleLog2 = 8.0f;         // move m only when it grows by > 2^8
+constexpr float kSumCap = 65536.0f;          // largest per-lane exp-sum of a tile kept as is
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -137,6 +139,18 @@ __device__ __forceinline__ float xhalf_min(float x) {
 __device__ __forceinline__ float xhalf_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// This lane's part of the exp-sum of one tile (its 16 keys per 32-key
+// block), in fp32: four independent chains, then their sum.
+template <int KB>
+__device__ __forceinline__ float lane_sum(const float (&p)[KB][16]) {
+  float ps[4] = {p[0][0], p[0][1], p[0][2], p[0][3]};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int e = (kb == 0 ? 4 : 0); e < 16; ++e) ps[e & 3] += p[kb][e];
+  return (ps[0] + ps[1]) + (ps[2] + ps[3]);
 }
 
 template <int D, bool kNegScale>
@@ -245,86 +259,111 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
     }
 
     // ---- S^T = K Q^T for kKB blocks of 32 keys ---------------------------
-    f32x16 sacc[G::kKB];
+    auto scores = [&](f32x16 (&sa)[G::kKB], const __bf16* kt) {
 #pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb) {
-      bf16x8 kf[G::kKSteps];
+      for (int kb = 0; kb < G::kKB; ++kb) {
+        bf16x8 kf[G::kKSteps];
 #pragma unroll
-      for (int s = 0; s < G::kKSteps; ++s)
-        kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + kb * 32 * D + koff[s]));
-      sacc[kb] = f32x16{};
+        for (int s = 0; s < G::kKSteps; ++s)
+          kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kb * 32 * D + koff[s]));
+        sa[kb] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < G::kKSteps; ++s) sacc[kb] = mfma32x32x16(kf[s], qf[s], sacc[kb]);
-    }
-
+        for (int s = 0; s < G::kKSteps; ++s) sa[kb] = mfma32x32x16(kf[s], qf[s], sa[kb]);
+      }
+    };
     // ---- online softmax on this lane's 16 * kKB scores -------------------
+    // Fast path (every full tile after the first): weights against the
+    // running max as it stands, p = 2^(s c - m), with no max over the tile.
+    // m only has to bound the weights, not equal the row max (any common
+    // shift of a row leaves its softmax unchanged), so the tile is kept as
+    // long as the lane's exp-sum over it stays <= kSumCap; that also bounds
+    // every weight.  Otherwise (first tile, tail tile, a sum above the cap,
+    // or not finite) the full step takes the tile's row max, moves m and
+    // rescales the accumulators first; it computes the scores itself, from
+    // the K tile still in LDS, so that the fast path need not keep its
+    // scores beside the weights for a tile that fails the cap.
     const int j0 = jt * G::kBc;
     const bool tail = j0 + G::kBc > N;
-    float ext;
-    if (!tail) {
-      // tree of max (min) over the lane's scores
-      float t[G::kKB * 4];
-#pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x16& a = sacc[kb];
-          t[kb * 4 + r] = kNegScale
-              ? vmin(vmin(a[4 * r], a[4 * r + 1]), vmin(a[4 * r + 2], a[4 * r + 3]))
-              : vmax(vmax(a[4 * r], a[4 * r + 1]), vmax(a[4 * r + 2], a[4 * r + 3]));
-        }
-#pragma unroll
-      for (int w = G::kKB * 4; w > 1; w >>= 1)
-#pragma unroll
-        for (int i = 0; i < w / 2; ++i)
-          t[i] = kNegScale ? vmin(t[i], t[i + w / 2]) : vmax(t[i], t[i + w / 2]);
-      ext = kNegScale ? xhalf_min(t[0]) : xhalf_max(t[0]);
-    } else {
-      // keys >= N (zero rows) are not part of the softmax: leave them out
-      float e2 = kNegScale ? INFINITY : -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key < N) e2 = kNegScale ? vmin(e2, sacc[kb][e]) : vmax(e2, sacc[kb][e]);
-        }
-      ext = kNegScale ? xhalf_min(e2) : xhalf_max(e2);
-    }
-    ext *= c_log2;   // the row's max of s * c_log2
-
-    // move the running max only when some row's max grows by > 2^kRescaleLog2
-    if (__any(ext > m_run + kRescaleLog2)) {
-      const float m_new = fmaxf(m_run, ext);
-      const float alpha = exp2_fast(m_run - m_new);   // 0 on the first tile
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < G::kDB; ++i) oacc[i] *= alpha;
-    }
-
     float p[G::kKB][16];
-#pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) p[kb][e] = exp2_fast(__builtin_fmaf(sacc[kb][e], c_log2, -m_run));
-    if (tail) {
-#pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key >= N) p[kb][e] = 0.0f;
-        }
-    }
-    {
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    float tsum;
+    bool redo = tail || jt == 0;
+    if (!redo) {
+      f32x16 sacc[G::kKB];
+      scores(sacc, ks);
 #pragma unroll
       for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ps[e & 3] += p[kb][e];
-      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        for (int e = 0; e < 16; ++e) p[kb][e] = exp2_fast(__builtin_fmaf(sacc[kb][e], c_log2, -m_run));
+      tsum = lane_sum<G::kKB>(p);
+      redo = __any(!(tsum <= kSumCap));
     }
+    if (redo) {
+      // the tile's offset goes through an empty asm statement so that the
+      // compiler cannot merge these reads and products with the ones above
+      int off = (jt & 1) * G::kStage;
+      asm volatile("" : "+s"(off));
+      f32x16 sre[G::kKB];
+      scores(sre, smem + off);
+      float ext;
+      if (!tail) {
+        // tree of max (min) over the lane's scores
+        float t[G::kKB * 4];
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const f32x16& a = sre[kb];
+            t[kb * 4 + r] = kNegScale
+                ? vmin(vmin(a[4 * r], a[4 * r + 1]), vmin(a[4 * r + 2], a[4 * r + 3]))
+                : vmax(vmax(a[4 * r], a[4 * r + 1]), vmax(a[4 * r + 2], a[4 * r + 3]));
+          }
+#pragma unroll
+        for (int w = G::kKB * 4; w > 1; w >>= 1)
+#pragma unroll
+          for (int i = 0; i < w / 2; ++i)
+            t[i] = kNegScale ? vmin(t[i], t[i + w / 2]) : vmax(t[i], t[i + w / 2]);
+        ext = kNegScale ? xhalf_min(t[0]) : xhalf_max(t[0]);
+      } else {
+        // keys >= N (zero rows) are not part of the softmax: leave them out
+        float e2 = kNegScale ? INFINITY : -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (key < N) e2 = kNegScale ? vmin(e2, sre[kb][e]) : vmax(e2, sre[kb][e]);
+          }
+        ext = kNegScale ? xhalf_min(e2) : xhalf_max(e2);
+      }
+      ext *= c_log2;   // the row's max of s * c_log2
+
+      // m moves up to the row max seen so far (never down); the rescale
+      // factor is 0 on the first tile, 1 for rows whose max did not grow
+      if (__any(ext > m_run)) {
+        const float m_new = fmaxf(m_run, ext);
+        const float alpha = exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < G::kDB; ++i) oacc[i] *= alpha;
+      }
+
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[kb][e] = exp2_fast(__builtin_fmaf(sre[kb][e], c_log2, -m_run));
+      if (tail) {
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (key >= N) p[kb][e] = 0.0f;
+          }
+      }
+      tsum = lane_sum<G::kKB>(p);
+    }
+    l_run += tsum;
 
     // ---- O^T += V^T P^T ---------------------------------------------------
     // P^T slot (hh, e) of k-step s2 in block kb holds key

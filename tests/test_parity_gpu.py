@@ -187,6 +187,27 @@ def test_fused_wide_inputs(attn):
     _check_full(attn, q, k, v, 1.0 / 8, torch.bfloat16, "wide scores")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("pattern", ["ramp", "steps", "falling"])
+def test_fused_moving_max(attn, pattern, d):
+    """Row maxima that keep growing along the keys (a ramp of key norms, or
+    each 64-key tile's keys doubled against the previous tile's), so the
+    kernels' bound on the weights keeps failing mid-row and the running max
+    is moved and the accumulators rescaled on later tiles; and the reverse,
+    maxima that only fall, where the first tile's max bounds the rest."""
+    N = 1000
+    q, k, v = workloads.random_inputs(1, 2, 1, N, d, torch.bfloat16, seed=41)
+    j = torch.arange(N, dtype=torch.float32)
+    if pattern == "ramp":
+        f = 1.0 + j / 64.0
+    elif pattern == "steps":
+        f = 2.0 ** torch.clamp(j // 64, max=6)
+    else:
+        f = 2.0 ** -torch.clamp(j // 64, max=6) * 8.0
+    k = (k.float() * f[None, None, :, None]).to(torch.bfloat16)
+    _check_full(attn, q, k, v, 1.0 / math.sqrt(d), torch.bfloat16, f"moving max {pattern}")
+
+
 # ---------------------------------------------------------------------------
 # invariants through the GPU
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
