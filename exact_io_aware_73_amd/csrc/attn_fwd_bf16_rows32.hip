@@ -42,6 +42,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -249,11 +251,14 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
   wait_dma();
   __syncthreads();
 
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const __bf16* ks = smem + (jt & 1) * G::kStage;
+  // One key tile in LDS stage `stage` (a compile-time constant: the loop
+  // below runs two tiles per trip, so every LDS read has a fixed offset).
+  auto tile = [&](const int jt, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
+    const __bf16* ks = smem + stage * G::kStage;
     const __bf16* vs = ks + G::kTile;
     if (jt + 1 < n_tiles) {
-      const uint32_t nxt = lds + ((jt + 1) & 1) * G::kStage * 2;
+      const uint32_t nxt = lds + (1 - stage) * G::kStage * 2;
       dma_tile<D>(kh, (jt + 1) * G::kBc, N, nxt, wave, dvoff);
       dma_tile<D>(vh, (jt + 1) * G::kBc, N, nxt + G::kTile * 2, wave, dvoff);
     }
@@ -300,7 +305,7 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
     if (redo) {
       // the tile's offset goes through an empty asm statement so that the
       // compiler cannot merge these reads and products with the ones above
-      int off = (jt & 1) * G::kStage;
+      int off = stage * G::kStage;
       asm volatile("" : "+s"(off));
       f32x16 sre[G::kKB];
       scores(sre, smem + off);
@@ -391,6 +396,10 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
 
     wait_dma();
     __syncthreads();
+  };
+  for (int jt = 0; jt < n_tiles; jt += 2) {
+    tile(jt, std::integral_constant<int, 0>{});
+    if (jt + 1 < n_tiles) tile(jt + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2 ------------------------
