@@ -30,17 +30,23 @@ import workloads  # noqa: E402
 from exact_io_aware_73_amd import accounting as acc  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak; HBM bytes vs Q/K/V/O min"
-KERNEL_SOURCES = ["exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows32.hip",
-                  "exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows64.hip",
-                  "exact_io_aware_73_amd/csrc/rows64_pipeline.hpp",
-                  "exact_io_aware_73_amd/csrc/attn_fwd_f32.hip",
-                  "exact_io_aware_73_amd/csrc/device_common.hpp",
-                  "exact_io_aware_73_amd/build.py"]
+# the sources each workload's fused kernel is built from, by I/O dtype and head dim
+_COMMON_SOURCES = ["exact_io_aware_73_amd/csrc/device_common.hpp", "exact_io_aware_73_amd/build.py"]
+KERNEL_SOURCES = {
+    ("bf16", 64): ["exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows32.hip"],
+    ("bf16", 128): ["exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows64.hip",
+                    "exact_io_aware_73_amd/csrc/rows64_pipeline.hpp"],
+    ("f32", 64): ["exact_io_aware_73_amd/csrc/attn_fwd_f32.hip"],
+    ("f32", 128): ["exact_io_aware_73_amd/csrc/attn_fwd_f32.hip"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str) -> str:
+    """Hash of the sources of the kernel that runs `workload` (a counter
+    summary taken on other sources no longer describes that kernel)."""
+    w = workloads.WORKLOADS[workload]
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[(w.dtype, w.d)] + _COMMON_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -54,7 +60,7 @@ def traffic_from_profiles(workload: str, per_launch_flops: int):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != kernel_source_hash():
+    if rec.get("kernel_source_sha") != kernel_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -296,7 +302,7 @@ def main():
         "backward": backward,
         "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
-        "kernel_source_sha": kernel_source_hash(),
+        "kernel_source_sha": kernel_source_hash(w.name),
     }
     print(json.dumps(out), flush=True)
 
