@@ -590,7 +590,10 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
 #pragma unroll
   for (int t = 0; t < kSlots - 2; ++t)
     dma_tile<D>(w.dvoff, vh, t * kBc, ATTN_KEYS, lds + (kSlots + t) * kTileB, wave);
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((2 * kSlots - 3) * G::kDma) : "memory");
+  // K tiles 0 and 1 must have landed: S of tile 0 reads K slot 0 here and
+  // step 0 reads K slot 1 (for S of tile 1) before its own wait; the other
+  // 2 kSlots - 4 tiles may still be in flight
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((2 * kSlots - 4) * G::kDma) : "memory");
 #pragma unroll
   for (int st = 0; st < G::kKSteps; ++st) {
     const bf16x8 kf = lds_k(lds, w.koff[st]);
