@@ -343,8 +343,11 @@ void attn_fwd_bf16_rows32_kernel(const __bf16* __restrict__ q, const __bf16* __r
       ext *= c_log2;   // the row's max of s * c_log2
 
       // m moves up to the row max seen so far (never down); the rescale
-      // factor is 0 on the first tile, 1 for rows whose max did not grow
-      if (__any(ext > m_run)) {
+      // factor is 1 for rows whose max did not grow.  On the first tile
+      // there is nothing to rescale yet (O and l are zero).
+      if (jt == 0) {
+        m_run = ext;
+      } else if (__any(ext > m_run)) {
         const float m_new = fmaxf(m_run, ext);
         const float alpha = exp2_fast(m_run - m_new);
         m_run = m_new;
