@@ -1,10 +1,13 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
     python -m exact_io_aware_73_amd.profiling stats  <trace_kernel_stats.csv> <out.txt> "<command>"
+        [<trace_kernel_trace.csv> <last_k>]
     python -m exact_io_aware_73_amd.profiling counters <workload> <fetch.csv> <write.csv>
         <copy_fetch.csv> <copy_write.csv> <copy_mib> <out.json> "<commands>"
 
-``stats`` turns a ``--kernel-trace --stats`` CSV into a short text table.
+``stats`` turns a ``--kernel-trace --stats`` CSV into a short text table;
+given the per-dispatch trace and K, it adds each kernel's mean over its
+last K dispatches (the timed steps of a bench run, after its warm-up).
 ``counters`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
 the fused kernel, and the same two counters read on a plain device copy of
 known size, into HBM bytes per launch: each counter (KiB per dispatch) is
@@ -34,6 +37,23 @@ def kernel_stats_table(path: str, command: str) -> str:
     lines.append("")
     lines.append("full kernel names:")
     lines += [f"  {r['Name']}" for r in rows]
+    return "\n".join(lines) + "\n"
+
+
+def last_k_table(trace_path: str, last_k: int) -> str:
+    """Mean / min / max duration of each kernel's last `last_k` dispatches."""
+    by_name = {}
+    for r in csv.DictReader(open(trace_path)):
+        by_name.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    lines = ["", f"last {last_k} dispatches of each kernel (the timed steps):",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+    for name, ds in by_name.items():
+        ds.sort()
+        tail = [d for _, d in ds[-last_k:]]
+        short = name if len(name) <= 60 else name[:57] + "..."
+        lines.append(f"{short:60s} {len(tail):6d} {statistics.mean(tail) / 1e3:10.1f} "
+                     f"{min(tail) / 1e3:10.1f} {max(tail) / 1e3:10.1f}")
     return "\n".join(lines) + "\n"
 
 
@@ -69,8 +89,11 @@ def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_
 
 def main(argv):
     if argv[0] == "stats":
-        _, src, out, cmd = argv
-        open(out, "w").write(kernel_stats_table(src, cmd))
+        src, out, cmd = argv[1:4]
+        text = kernel_stats_table(src, cmd)
+        if len(argv) > 4:
+            text += last_k_table(argv[4], int(argv[5]))
+        open(out, "w").write(text)
     elif argv[0] == "counters":
         _, wl, f, w, cf, cw, mib, out, cmds, sha = argv
         rec = counters_summary(wl, f, w, cf, cw, int(mib), cmds, sha)
