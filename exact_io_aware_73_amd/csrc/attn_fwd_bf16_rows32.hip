@@ -442,9 +442,9 @@ uint64_t fwd_bf16_rows32_grid(int B, int Hq, int Hkv, int N) {
 }
 
 hipError_t launch_fwd_bf16_rows32(const FwdArgs& a) {
-  const bool neg = a.scale < 0.0f;
-  if (a.d == 128) return neg ? launch_d<128, true>(a) : launch_d<128, false>(a);
-  return neg ? launch_d<64, true>(a) : launch_d<64, false>(a);
+  // head dim 64 only (head dim 128 runs the rows64 kernel)
+  if (a.d != 64) return hipErrorInvalidValue;
+  return a.scale < 0.0f ? launch_d<64, true>(a) : launch_d<64, false>(a);
 }
 
 }  // namespace attn

@@ -36,8 +36,8 @@ uint64_t fwd_bf16_rows64_grid(int B, int Hq, int Hkv, int N);
 uint64_t fwd_f32_grid(int B, int Hq, int N);
 
 // Fused bf16 forward, two kernel designs:
-//   rows32 -- one 32-row query block per wave, two workgroups per CU
-//             (head dim 64: the softmax, not LDS, bounds it there);
+//   rows32 -- one 32-row query block per wave, four workgroups per CU
+//             (head dim 64 only: the softmax, not LDS, bounds it there);
 //   rows64 -- two 32-row query blocks per wave sharing every K / V fragment
 //             read from LDS, software-pipelined across key tiles (head dim
 //             128, where LDS bandwidth bounds the one-block layout).
