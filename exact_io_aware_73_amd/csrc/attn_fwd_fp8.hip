@@ -35,6 +35,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -240,11 +242,14 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restric
   wait_dma();
   __syncthreads();
 
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const uint8_t* ks = smem + (jt & 1) * G::kStageB;
+  // One key tile in LDS stage `stage` (a compile-time constant: the loop
+  // below runs two tiles per trip, so every LDS read has a fixed offset).
+  auto tile = [&](const int jt, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
+    const uint8_t* ks = smem + stage * G::kStageB;
     const uint8_t* vs = ks + G::kTileB;
     if (jt + 1 < n_tiles) {
-      const uint32_t nxt = lds + (uint32_t)(((jt + 1) & 1) * G::kStageB);
+      const uint32_t nxt = lds + (uint32_t)((1 - stage) * G::kStageB);
       dma_k<D>(kh, (jt + 1) * kBc, N, nxt, wave, koff_dma);
       dma_vt<D>(vh, (jt + 1) * kBc, Np, nxt + G::kTileB, wave, voff_dma);
     }
@@ -366,6 +371,10 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restric
 
     wait_dma();
     __syncthreads();
+  };
+  for (int jt = 0; jt < n_tiles; jt += 2) {
+    tile(jt, std::integral_constant<int, 0>{});
+    if (jt + 1 < n_tiles) tile(jt + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = v_scale * O~ / l, lse = (m + log2 l - 6) ln 2 ----------
