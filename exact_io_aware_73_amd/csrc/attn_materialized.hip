@@ -141,6 +141,70 @@ void softmax_rows_kernel(const float* __restrict__ s, OutT* __restrict__ p, floa
   if (tid == 0) lse[row] = m + logf(l);
 }
 
+// The same with 16-byte accesses (rows of N % 4 == 0 floats are 16-byte
+// aligned): each thread takes whole 4-score chunks, keeping (max, exp-sum)
+// per chunk rather than per score, and writes its 4 weights at once.
+template <typename OutT>
+__device__ __forceinline__ void store_p4(OutT* p, int64_t i, f32x4 x);
+template <>
+__device__ __forceinline__ void store_p4<float>(float* p, int64_t i, f32x4 x) {
+  *reinterpret_cast<f32x4*>(p + i) = x;
+}
+template <>
+__device__ __forceinline__ void store_p4<__bf16>(__bf16* p, int64_t i, f32x4 x) {
+  u32x2 w;
+  w[0] = pack_bf16x2(x[0], x[1]);
+  w[1] = pack_bf16x2(x[2], x[3]);
+  *reinterpret_cast<u32x2*>(p + i) = w;
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256)
+void softmax_rows_vec_kernel(const float* __restrict__ s, OutT* __restrict__ p,
+                             float* __restrict__ lse, int N) {
+  __shared__ float red_m[4], red_l[4];
+  const int64_t row = blockIdx.x;
+  const float* srow = s + row * (int64_t)N;
+  const int tid = threadIdx.x;
+  const int n4 = N / 4;
+  constexpr float kL2e = 1.44269504088896341f;
+
+  float m = -INFINITY, l = 0.0f;
+  for (int j = tid; j < n4; j += 256) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(srow + 4 * j);
+    const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    const float mn = fmaxf(m, mx);
+    const float part = exp2_fast((x[0] - mn) * kL2e) + exp2_fast((x[1] - mn) * kL2e) +
+                       exp2_fast((x[2] - mn) * kL2e) + exp2_fast((x[3] - mn) * kL2e);
+    l = (m == -INFINITY ? 0.0f : l * exp2_fast((m - mn) * kL2e)) + part;
+    m = mn;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float l2 = __shfl_xor(l, off);
+    merge_ml(m, l, m2, l2);
+  }
+  if ((tid & 63) == 0) {
+    red_m[tid >> 6] = m;
+    red_l[tid >> 6] = l;
+  }
+  __syncthreads();
+  m = red_m[0];
+  l = red_l[0];
+  for (int w = 1; w < 4; ++w) merge_ml(m, l, red_m[w], red_l[w]);
+
+  const float inv = 1.0f / l;
+  OutT* prow = p + row * (int64_t)N;
+  for (int j = tid; j < n4; j += 256) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(srow + 4 * j);
+    f32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = exp2_fast((x[i] - m) * kL2e) * inv;
+    store_p4<OutT>(prow, 4 * (int64_t)j, y);
+  }
+  if (tid == 0) lse[row] = m + logf(l);
+}
+
 // ---------------------------------------------------------------------------
 // O = P V, bf16: one workgroup per 128 query rows of a head.  V tiles are
 // staged transposed through LDS (shared staging with the fused kernel); P^T
@@ -337,8 +401,12 @@ hipError_t launch_bf16_d(const FwdArgs& a) {
                      static_cast<const __bf16*>(a.k), a.s, a.Hq, a.Hkv, a.N, a.scale, n_t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((softmax_rows_kernel<__bf16>), dim3((uint32_t)rows), dim3(256), 0, a.stream,
-                     a.s, static_cast<__bf16*>(a.p), a.lse, a.N);
+  if (a.N % 4 == 0)
+    hipLaunchKernelGGL((softmax_rows_vec_kernel<__bf16>), dim3((uint32_t)rows), dim3(256), 0,
+                       a.stream, a.s, static_cast<__bf16*>(a.p), a.lse, a.N);
+  else
+    hipLaunchKernelGGL((softmax_rows_kernel<__bf16>), dim3((uint32_t)rows), dim3(256), 0, a.stream,
+                       a.s, static_cast<__bf16*>(a.p), a.lse, a.N);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (a.N + kBr - 1) / kBr;
@@ -364,8 +432,12 @@ hipError_t launch_f32_d(const FwdArgs& a) {
                      a.s, a.Hq, a.Hkv, a.N, D, a.scale, n_t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((softmax_rows_kernel<float>), dim3((uint32_t)rows), dim3(256), 0, a.stream,
-                     a.s, static_cast<float*>(a.p), a.lse, a.N);
+  if (a.N % 4 == 0)
+    hipLaunchKernelGGL((softmax_rows_vec_kernel<float>), dim3((uint32_t)rows), dim3(256), 0,
+                       a.stream, a.s, static_cast<float*>(a.p), a.lse, a.N);
+  else
+    hipLaunchKernelGGL((softmax_rows_kernel<float>), dim3((uint32_t)rows), dim3(256), 0, a.stream,
+                       a.s, static_cast<float*>(a.p), a.lse, a.N);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pv_f32_kernel<D>), dim3((uint32_t)((uint64_t)n_t * a.B * a.Hq)), dim3(256), 0,
