@@ -205,6 +205,56 @@ void softmax_rows_vec_kernel(const float* __restrict__ s, OutT* __restrict__ p,
   if (tid == 0) lse[row] = m + logf(l);
 }
 
+// Rows of at most kWaveRowMax scores (N % 4 == 0): one wave per row, the
+// row held in registers (16-byte loads, up to 16 per lane), so S is read
+// from memory once; max and exp-sum by wave reductions.
+constexpr int kWaveRowChunks = 16;                       // 4-score chunks per lane
+constexpr int kWaveRowMax = kWaveRowChunks * 4 * kWave;  // 4096 scores
+
+template <typename OutT>
+__global__ __launch_bounds__(256)
+void softmax_rows_wave_kernel(const float* __restrict__ s, OutT* __restrict__ p,
+                              float* __restrict__ lse, int N, int64_t n_rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const float* srow = s + row * (int64_t)N;
+  constexpr float kL2e = 1.44269504088896341f;
+  const int n4 = N / 4;
+
+  f32x4 x[kWaveRowChunks];
+  float m = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kWaveRowChunks; ++c) {
+    const int j = c * kWave + lane;
+    if (j < n4) {
+      x[c] = *reinterpret_cast<const f32x4*>(srow + 4 * j);
+      m = fmaxf(m, fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3])));
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float l = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kWaveRowChunks; ++c) {
+    if (c * kWave + lane < n4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[c][i] = exp2_fast((x[c][i] - m) * kL2e);
+        l += x[c][i];
+      }
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+  const float inv = 1.0f / l;
+  OutT* prow = p + row * (int64_t)N;
+#pragma unroll
+  for (int c = 0; c < kWaveRowChunks; ++c) {
+    const int j = c * kWave + lane;
+    if (j < n4) store_p4<OutT>(prow, 4 * (int64_t)j, x[c] * inv);
+  }
+  if (lane == 0) lse[row] = m + logf(l);
+}
+
 // ---------------------------------------------------------------------------
 // O = P V, bf16: one workgroup per 128 query rows of a head.  V tiles are
 // staged transposed through LDS (shared staging with the fused kernel); P^T
@@ -401,7 +451,11 @@ hipError_t launch_bf16_d(const FwdArgs& a) {
                      static_cast<const __bf16*>(a.k), a.s, a.Hq, a.Hkv, a.N, a.scale, n_t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.N % 4 == 0)
+  if (a.N % 4 == 0 && a.N <= kWaveRowMax)
+    hipLaunchKernelGGL((softmax_rows_wave_kernel<__bf16>), dim3((uint32_t)((rows + 3) / 4)),
+                       dim3(256), 0, a.stream, a.s, static_cast<__bf16*>(a.p), a.lse, a.N,
+                       (int64_t)rows);
+  else if (a.N % 4 == 0)
     hipLaunchKernelGGL((softmax_rows_vec_kernel<__bf16>), dim3((uint32_t)rows), dim3(256), 0,
                        a.stream, a.s, static_cast<__bf16*>(a.p), a.lse, a.N);
   else
@@ -432,7 +486,11 @@ hipError_t launch_f32_d(const FwdArgs& a) {
                      a.s, a.Hq, a.Hkv, a.N, D, a.scale, n_t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.N % 4 == 0)
+  if (a.N % 4 == 0 && a.N <= kWaveRowMax)
+    hipLaunchKernelGGL((softmax_rows_wave_kernel<float>), dim3((uint32_t)((rows + 3) / 4)),
+                       dim3(256), 0, a.stream, a.s, static_cast<float*>(a.p), a.lse, a.N,
+                       (int64_t)rows);
+  else if (a.N % 4 == 0)
     hipLaunchKernelGGL((softmax_rows_vec_kernel<float>), dim3((uint32_t)rows), dim3(256), 0,
                        a.stream, a.s, static_cast<float*>(a.p), a.lse, a.N);
   else
