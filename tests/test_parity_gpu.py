@@ -305,8 +305,12 @@ def test_python_rejects_bad_arguments(attn):
 # ---------------------------------------------------------------------------
 # materialising path: O, lse, and the S and P it writes
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+# N covers the three row-softmax kernels of the comparison path: N % 4 != 0
+# (one score per thread), N % 4 == 0 up to 4096 (one wave per row, from
+# registers) and beyond (two passes of 16-byte loads)
 @pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 1, 1, 1, 64), (1, 2, 1, 37, 64), (2, 4, 2, 129, 128),
-                                           (1, 2, 2, 256, 64), (1, 4, 1, 300, 128), (1, 1, 1, 1000, 64)])
+                                           (1, 2, 2, 256, 64), (1, 4, 1, 300, 128), (1, 1, 1, 1000, 64),
+                                           (1, 1, 1, 4100, 64)])
 def test_materialized_small(attn, dtype, B, Hq, Hkv, N, d):
     q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, dtype, seed=13 * N + d)
     scale = 1 / math.sqrt(d)
