@@ -52,10 +52,11 @@ def kernel_source_hash(workload: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str, per_launch_flops: int):
+def traffic_from_profiles(workload: str, per_launch_flops: int, profiles_dir: str | None = None):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload, or None when absent or taken on other kernel source."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_counters.json")
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"),
+                        f"attn_fwd_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:

@@ -1,0 +1,75 @@
+"""Host logic of the profile summaries and the bench's counter matching (CPU only)."""
+from __future__ import annotations
+
+import csv
+import json
+
+import pytest
+
+from exact_io_aware_73_amd import profiling
+
+TRACE_FIELDS = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+
+
+def _write_trace(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=TRACE_FIELDS)
+        w.writeheader()
+        for name, start, dur in rows:
+            w.writerow({"Kind": "KERNEL_DISPATCH", "Kernel_Name": name,
+                        "Start_Timestamp": start, "End_Timestamp": start + dur})
+
+
+def test_last_k_takes_the_latest_dispatches(tmp_path):
+    # warm-up dispatches are slow (900 us), the timed ones ~100 us, written out of order
+    rows = [("fused", 10_000_000 + 1_000_000 * i, 900_000) for i in range(5)]
+    rows += [("fused", 20_000_000 + 1_000_000 * i, 100_000 + 1000 * i) for i in range(3)]
+    rows += [("other", 5_000_000, 50_000)]
+    path = tmp_path / "trace.csv"
+    _write_trace(path, list(reversed(rows)))
+    text = profiling.last_k_table(str(path), 3)
+    line = next(ln for ln in text.splitlines() if ln.startswith("fused"))
+    calls, avg, lo, hi = line.split()[1:]
+    assert int(calls) == 3
+    assert float(avg) == pytest.approx(101.0)                  # microseconds
+    assert float(lo) == pytest.approx(100.0) and float(hi) == pytest.approx(102.0)
+    other = next(ln for ln in text.splitlines() if ln.startswith("other"))
+    assert int(other.split()[1]) == 1                          # fewer dispatches than K
+
+
+def _counter_csv(path, kernel, values):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Value"])
+        w.writeheader()
+        for v in values:
+            w.writerow({"Kernel_Name": kernel, "Counter_Value": v})
+
+
+def test_counters_scale_by_the_copy_calibration(tmp_path):
+    # a 1 MiB copy reads as 512 KiB fetched and 1024 KiB written: fetch x2, write x1
+    _counter_csv(tmp_path / "cf.csv", profiling.COPY_KERNEL, [512.0, 512.0, 512.0])
+    _counter_csv(tmp_path / "cw.csv", profiling.COPY_KERNEL, [1024.0])
+    _counter_csv(tmp_path / "f.csv", profiling.FUSED_KERNEL + "_kernel<64>", [100.0, 101.0, 99.0])
+    _counter_csv(tmp_path / "w.csv", profiling.FUSED_KERNEL + "_kernel<64>", [50.0])
+    rec = profiling.counters_summary("wl", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                     str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), 1,
+                                     "cmd", "sha")
+    assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
+    assert rec["hbm_read_bytes_per_launch"] == 100 * 1024 * 2      # the median dispatch
+    assert rec["hbm_write_bytes_per_launch"] == 50 * 1024
+    assert rec["hbm_bytes_per_launch"] == 100 * 1024 * 2 + 50 * 1024
+
+
+def test_counter_summary_matches_only_its_own_kernel_sources(tmp_path):
+    import bench
+
+    w = "gpt2_medium_b64_h16_n1024_d64"
+    rec = {"kernel_source_sha": bench.kernel_source_hash(w), "hbm_bytes_per_launch": 12345}
+    path = tmp_path / f"attn_fwd_{w}_counters.json"
+    path.write_text(json.dumps(rec))
+    assert bench.traffic_from_profiles(w, 0, str(tmp_path)) == 12345
+    path.write_text(json.dumps(dict(rec, kernel_source_sha="stale")))
+    assert bench.traffic_from_profiles(w, 0, str(tmp_path)) is None
+    assert bench.traffic_from_profiles("long_b4_h32_n4096_d128", 0, str(tmp_path)) is None
+    # the d = 64 and d = 128 kernels are built from different sources
+    assert bench.kernel_source_hash(w) != bench.kernel_source_hash("long_b4_h32_n4096_d128")
