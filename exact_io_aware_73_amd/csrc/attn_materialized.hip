@@ -23,9 +23,8 @@ namespace {
 // ---------------------------------------------------------------------------
 // S = scale * Q K^T, bf16 inputs, one workgroup per 128 x 128 block of S.
 // Wave w computes queries [qt*128 + 32 w, +32) x keys [kt*128, +128) as four
-// S^T blocks (K as the A operand read straight from global memory, Q^T as
-// the B operand in VGPRs); lane (query l%32, half h) then holds keys
-// 8 r + 4 h + {0..3} of its query row for r = 0..3.
+// 32 x 32 S blocks (Q as the A operand in VGPRs, K^T as the B operand read
+// straight from global memory).
 template <int D>
 __global__ __launch_bounds__(kThreads)
 void qk_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -50,34 +49,34 @@ void qk_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                        : u32x4{0u, 0u, 0u, 0u};
     qf[st] = as_bf16x8(u);
   }
-  const bool vec = (N % 4) == 0;
-#pragma unroll 1
+  // All four key blocks' K operands are loaded before the first product,
+  // and S (not S^T) is accumulated: with Q as the A operand a lane holds one
+  // key of 16 queries, so each store writes 128 contiguous bytes of two rows.
+  bf16x8 kf[4][kSteps];
+#pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const int kbase = kt * 128 + kb * 32;
-    const int krow = kbase + l32;
-    f32x16 acc = f32x16{};
+    const int krow = kt * 128 + kb * 32 + l32;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       u32x4 u = krow < N ? *reinterpret_cast<const u32x4*>(kh + (int64_t)krow * D + 16 * st + 8 * hh)
                          : u32x4{0u, 0u, 0u, 0u};
-      acc = mfma32x32x16(as_bf16x8(u), qf[st], acc);
+      kf[kb][st] = as_bf16x8(u);
     }
-    if (qrow < N) {
-      float* srow = sh + (int64_t)qrow * N;
+  }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kbase + 8 * r + 4 * hh;
-        const f32x4 val = {acc[4 * r] * scale, acc[4 * r + 1] * scale, acc[4 * r + 2] * scale,
-                           acc[4 * r + 3] * scale};
-        if (vec && key + 3 < N) {
-          *reinterpret_cast<f32x4*>(srow + key) = val;
-        } else {
+  for (int kb = 0; kb < 4; ++kb) {
+    const int key = kt * 128 + kb * 32 + l32;          // this lane's key
+    f32x16 acc = f32x16{};
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            if (key + t < N) srow[key + t] = val[t];
-        }
+    for (int st = 0; st < kSteps; ++st) acc = mfma32x32x16(qf[st], kf[kb][st], acc);
+    // element 4 r + t of a lane is S[query 8 r + 4 hh + t of the wave][key]
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int qr = qt * 128 + wave * 32 + 8 * r + 4 * hh + t;
+        if (qr < N && key < N) sh[(int64_t)qr * N + key] = acc[4 * r + t] * scale;
       }
-    }
   }
 }
 
