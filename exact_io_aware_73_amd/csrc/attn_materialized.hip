@@ -284,30 +284,52 @@ void pv_bf16_kernel(const __bf16* __restrict__ p, const __bf16* __restrict__ v,
 #pragma unroll
   for (int i = 0; i < G::kDB; ++i) oacc[i] = f32x16{};
 
-  const int n_tiles = (N + G::kBc - 1) / G::kBc;
-  Regs regs;
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const int j0 = jt * G::kBc;
-    load_v_tile<D>(regs, vh, j0, N, tid);
-    store_v_tile<D>(regs, vts, tid);
-    __syncthreads();
+  // P^T fragments of one tile: slot (hh, e) of k-step s2 in block kb is key
+  // j0 + kb * 32 + 16 s2 + 8 hh + e of this lane's row
+  auto load_p = [&](u32x4 (&pu)[G::kKB][2], int j0) {
 #pragma unroll
     for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int key0 = j0 + kb * 32 + 16 * s2 + 8 * hh;   // slot (hh, e) = key key0 + e
-        u32x4 pu;
+        const int key0 = j0 + kb * 32 + 16 * s2 + 8 * hh;
         if (kVecP && qvalid && key0 + 7 < N) {
-          pu = *reinterpret_cast<const u32x4*>(prow + key0);
+          pu[kb][s2] = *reinterpret_cast<const u32x4*>(prow + key0);
         } else {
           uint16_t hw[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             hw[e] = (qvalid && key0 + e < N) ? reinterpret_cast<const uint16_t*>(prow)[key0 + e] : 0;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) pu[w] = (uint32_t)hw[2 * w] | ((uint32_t)hw[2 * w + 1] << 16);
+          for (int w = 0; w < 4; ++w)
+            pu[kb][s2][w] = (uint32_t)hw[2 * w] | ((uint32_t)hw[2 * w + 1] << 16);
         }
-        const bf16x8 pf = as_bf16x8(pu);
+      }
+  };
+
+  // The next tile's V (through registers) and P fragments are loaded while
+  // the current tile's products run.
+  const int n_tiles = (N + G::kBc - 1) / G::kBc;
+  Regs regs;
+  u32x4 pn[G::kKB][2];
+  load_v_tile<D>(regs, vh, 0, N, tid);
+  load_p(pn, 0);
+  for (int jt = 0; jt < n_tiles; ++jt) {
+    store_v_tile<D>(regs, vts, tid);
+    __syncthreads();
+    u32x4 pc[G::kKB][2];
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) pc[kb][s2] = pn[kb][s2];
+    if (jt + 1 < n_tiles) {
+      load_v_tile<D>(regs, vh, (jt + 1) * G::kBc, N, tid);
+      load_p(pn, (jt + 1) * G::kBc);
+    }
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 pf = as_bf16x8(pc[kb][s2]);
 #pragma unroll
         for (int db = 0; db < G::kDB; ++db) {
           const __bf16* vr = vts + (db * 32 + l32) * G::kVStr + kb * 32 + 16 * s2 + 8 * hh;
