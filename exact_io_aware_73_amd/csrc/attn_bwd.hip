@@ -215,9 +215,13 @@ void attn_bwd_rowdot_kernel(const __bf16* __restrict__ o, const __bf16* __restri
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per 128 keys of K/V head (b, kvh).
-template <int D>
-__global__ __launch_bounds__(kBThreads, D == 64 ? 2 : 1)
+// dK, dV: one workgroup per 128 keys of K/V head (b, kvh).  kOut picks the
+// outputs: both (0), dV only (1) or dK only (2).  At head dim 128 both at
+// once need 368 registers (one wave per SIMD, latency-bound); apart, the dV
+// pass (S and dV products, 180 registers) and the dK pass (S, dP and dK,
+// 240) each run two waves per SIMD.
+template <int D, int kOut>
+__global__ __launch_bounds__(kBThreads, D == 64 || kOut != 0 ? 2 : 1)
 void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                           const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                           const float* __restrict__ lse, const float* __restrict__ dvec,
@@ -249,9 +253,10 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   const int64_t head_q = ((int64_t)b * Hkv + kvh) * (int64_t)n_qrows;
 
   const int krow = kt * kWgRows + wave * kWRows + l32;   // this lane's key (B operand column)
+  constexpr bool kDV = kOut != 2, kDK = kOut != 1;
   bf16x8 kf[G::kKSteps], vf[G::kKSteps];
   load_rowfrags<D>(kf, k + head_kv * D, krow, N, hh);
-  load_rowfrags<D>(vf, v + head_kv * D, krow, N, hh);
+  if (kDK) load_rowfrags<D>(vf, v + head_kv * D, krow, N, hh);
 
   const TileOffsets<D> off = tile_offsets<D>(lane, wave);
   f32x16 dkacc[G::kDB], dvacc[G::kDB];
@@ -311,9 +316,11 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
 #pragma unroll
         for (int s = 0; s < G::kKSteps; ++s) {
           const bf16x8 qa = lds_row(qtile + qb * 32 * D * 2, off.row[s]);
-          const bf16x8 da = lds_row(dotile + qb * 32 * D * 2, off.row[s]);
           sacc[qb] = mfma32x32x16(qa, kf[s], sacc[qb]);
-          pacc[qb] = mfma32x32x16(da, vf[s], pacc[qb]);
+          if (kDK) {
+            const bf16x8 da = lds_row(dotile + qb * 32 * D * 2, off.row[s]);
+            pacc[qb] = mfma32x32x16(da, vf[s], pacc[qb]);
+          }
         }
       }
 #pragma unroll
@@ -328,7 +335,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
           for (int j = 0; j < 4; ++j) {
             const int e = 4 * r + j;
             p[e] = exp2_fast(__builtin_fmaf(sacc[qb][e], c_log2, -l4[j]));
-            ds[e] = p[e] * (pacc[qb][e] - d4[j]);
+            ds[e] = kDK ? p[e] * (pacc[qb][e] - d4[j]) : 0.0f;
           }
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
@@ -343,8 +350,10 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
           const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
 #pragma unroll
           for (int db = 0; db < G::kDB; ++db) {
-            dvacc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), dvacc[db]);
-            dkacc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dkacc[db]);
+            if (kDV)
+              dvacc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), dvacc[db]);
+            if (kDK)
+              dkacc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dkacc[db]);
           }
         }
       }
@@ -398,8 +407,8 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   }
 
   if (krow < N) {
-    store_rowT<D>(dkacc, dk + (head_kv + krow) * D, scale, hh);
-    store_rowT<D>(dvacc, dv + (head_kv + krow) * D, 1.0f, hh);
+    if (kDK) store_rowT<D>(dkacc, dk + (head_kv + krow) * D, scale, hh);
+    if (kDV) store_rowT<D>(dvacc, dv + (head_kv + krow) * D, 1.0f, hh);
   }
 }
 
@@ -518,13 +527,19 @@ hipError_t launch_d(const FwdArgs& a, const BwdArgs& g) {
   if (e != hipSuccess) return e;
   const int n_kt = (a.N + kWgRows - 1) / kWgRows;
   const uint64_t grid1 = (uint64_t)n_kt * a.Hkv * a.B;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((uint32_t)grid1), dim3(kBThreads), 0, a.stream,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(g.dout), a.lse,
-                     g.dvec, static_cast<__bf16*>(g.dk), static_cast<__bf16*>(g.dv), a.Hq, a.Hkv,
-                     a.N, c_log2, a.scale, n_kt, (uint32_t)a.n_xcd);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // head dim 128: dV and dK in two passes (see the kernel); 64: one pass
+  constexpr int kPasses = D == 128 ? 2 : 1;
+  for (int pass = 0; pass < kPasses; ++pass) {
+    auto kern = D == 128 ? (pass == 0 ? attn_bwd_dkdv_kernel<D, 1> : attn_bwd_dkdv_kernel<D, 2>)
+                         : attn_bwd_dkdv_kernel<D, 0>;
+    hipLaunchKernelGGL(kern, dim3((uint32_t)grid1), dim3(kBThreads), 0, a.stream,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(g.dout), a.lse,
+                       g.dvec, static_cast<__bf16*>(g.dk), static_cast<__bf16*>(g.dv), a.Hq, a.Hkv,
+                       a.N, c_log2, a.scale, n_kt, (uint32_t)a.n_xcd);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int n_qt = (int)(((uint64_t)(a.Hq / a.Hkv) * a.N + kWgRows - 1) / kWgRows);
   const uint64_t grid2 = (uint64_t)n_qt * a.Hkv * a.B;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((uint32_t)grid2), dim3(kBThreads), 0, a.stream,
