@@ -1,0 +1,162 @@
+"""Tensors of more than 2^31 elements (byte offsets past 2^32) through every
+fused entry point, so that any offset computed in 32 bits would wrap.
+
+Shapes: N = 256 and B * H heads chosen so that B * H * N * d just exceeds
+2^31 (4.3 GB per bf16 tensor).  Every head is zero except the first and the
+last, which hold seeded random data and are checked against the oracle; the
+zero heads must give O = 0 (equal weights over zero V rows) and
+lse = ln N, and zero gradients.  A wrapped offset would make a checked head
+read zeros, or a zero head read the random data: either fails.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import compare, half_ulp
+
+pytestmark = pytest.mark.gpu
+
+N = 256
+SHAPES = {64: (32, 4097), 128: (16, 4097)}   # d -> (B, H): B * H * N * d > 2^31
+MIN_ELEMENTS = 2 ** 31
+DEVICE = "cuda"
+
+
+@pytest.fixture(scope="module")
+def attn():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from exact_io_aware_73_amd import attn as a   # fails loudly if libattn.so is missing
+    return a
+
+
+@pytest.fixture(autouse=True)
+def _free():
+    yield
+    torch.cuda.empty_cache()
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _big(B, H, d, seed):
+    """Zero [B, H, N, d] bf16 tensors q, k, v with random heads (0, 0) and
+    (B-1, H-1); returns the device tensors and the two random heads (CPU)."""
+    assert B * H * N * d > MIN_ELEMENTS
+    small = workloads.random_inputs(1, 2, 2, N, d, torch.bfloat16, seed=seed)
+    big = []
+    for t in small:
+        g = torch.zeros((B, H, N, d), dtype=torch.bfloat16, device=DEVICE)
+        g[0, 0].copy_(t[0, 0])
+        g[B - 1, H - 1].copy_(t[0, 1])
+        big.append(g)
+    return big, small
+
+
+def _zero_heads(B, H):
+    z = torch.ones((B, H), dtype=torch.bool, device=DEVICE)
+    z[0, 0] = False
+    z[B - 1, H - 1] = False
+    return z
+
+
+def _check_fwd(o, lse, small, scale, label):
+    B, H = o.shape[:2]
+    q, k, v = small
+    for i, (b, h) in enumerate([(0, 0), (B - 1, H - 1)]):
+        O_ref, l_ref = oracle.attention_head(workloads.to_f64(q[0, i]), workloads.to_f64(k[0, i]),
+                                             workloads.to_f64(v[0, i]), scale)
+        r = compare(workloads.to_f64(o[b, h].cpu()), lse[b, h].cpu().numpy(), O_ref, l_ref, "bf16")
+        assert r["ok"], (label, (b, h), r)
+    z = _zero_heads(B, H)
+    omax = o.abs().amax(dim=(2, 3))
+    assert (omax[z] == 0).all(), f"{label}: a zero head has O != 0"
+    lerr = (lse - math.log(N)).abs().amax(dim=2)
+    assert (lerr[z] <= 1e-5).all(), f"{label}: a zero head has lse != ln N"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_past_2_31_elements(attn, d):
+    B, H = SHAPES[d]
+    _say(f"[large] attn_fwd B={B} H={H} N={N} d={d}")
+    (q, k, v), small = _big(B, H, d, seed=900 + d)
+    scale = 1 / math.sqrt(d)
+    o, lse = attn.fwd(q, k, v, scale)
+    torch.cuda.synchronize()
+    _check_fwd(o, lse, small, scale, f"fwd d={d}")
+
+
+def test_split_past_2_31_elements(attn):
+    B, H = SHAPES[128]
+    _say(f"[large] attn_fwd_split B={B} H={H} N={N} d=128 n_split=2")
+    (q, k, v), small = _big(B, H, 128, seed=1000)
+    scale = 1 / math.sqrt(128)
+    o, lse = attn.fwd_split(q, k, v, 2, scale)
+    torch.cuda.synchronize()
+    _check_fwd(o, lse, small, scale, "split")
+
+
+def test_bwd_past_2_31_elements(attn):
+    B, H = SHAPES[128]
+    _say(f"[large] attn_bwd B={B} H={H} N={N} d=128")
+    (q, k, v), small = _big(B, H, 128, seed=1100)
+    dsmall = workloads.random_inputs(1, 2, 2, N, 128, torch.bfloat16, seed=1107)[0]
+    dout = torch.zeros_like(q)
+    dout[0, 0].copy_(dsmall[0, 0])
+    dout[B - 1, H - 1].copy_(dsmall[0, 1])
+    scale = 1 / math.sqrt(128)
+    o, lse = attn.fwd(q, k, v, scale)
+    grads = attn.bwd(q, k, v, o, lse, dout, scale)
+    torch.cuda.synchronize()
+    del o, lse
+    z = _zero_heads(B, H)
+    for name, g in zip(("dq", "dk", "dv"), grads):
+        assert (g.abs().amax(dim=(2, 3))[z] == 0).all(), f"zero head has {name} != 0"
+    sq, sk, sv = small
+    for i, (b, h) in enumerate([(0, 0), (B - 1, H - 1)]):
+        ref = oracle.attention_bwd_ref(*(workloads.to_f64(t[:, i:i + 1]) for t in (sq, sk, sv, dsmall)),
+                                       scale)
+        for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+            err = float(np.max(np.abs(workloads.to_f64(g[b, h].cpu()) - r[0, 0])))
+            tol = 1e-2 * float(np.max(np.abs(r))) + 1e-4
+            assert err <= tol, ((b, h), name, err, tol)
+
+
+def test_fp8_past_2_31_elements(attn):
+    B, H = SHAPES[128]
+    d = 128
+    _say(f"[large] attn_fwd_fp8 B={B} H={H} N={N} d={d}")
+    q8s, k8s, vt8s, qs, ks, vs = workloads.fp8_inputs(1, 2, 2, N, d, 1200)
+    Np = attn.fp8_padded_keys(N)
+    assert tuple(vt8s.shape) == (1, 2, d, Np)
+    big = []
+    for t, shape in ((q8s, (B, H, N, d)), (k8s, (B, H, N, d)), (vt8s, (B, H, d, Np))):
+        g = torch.zeros(shape, dtype=torch.uint8, device=DEVICE)   # code 0 is +0
+        g[0, 0].copy_(t[0, 0])
+        g[B - 1, H - 1].copy_(t[0, 1])
+        big.append(g)
+    assert B * H * N * d > MIN_ELEMENTS
+    scale = 1 / math.sqrt(d)
+    o, lse = attn.fwd_fp8(*big, qs, ks, vs, scale)
+    torch.cuda.synchronize()
+    del big
+    for i, (b, h) in enumerate([(0, 0), (B - 1, H - 1)]):
+        args = (q8s[:, i:i + 1].numpy(), k8s[:, i:i + 1].numpy(), vt8s[:, i:i + 1].numpy(),
+                qs, ks, vs, scale)
+        O, lse_ref = oracle.attention_fp8_ref(*args)
+        bound = oracle.fp8_error_bound(*args)
+        lb = oracle.fp8_lse_bound(*args)
+        got = workloads.to_f64(o[b, h].cpu())
+        assert np.all(np.abs(got - O[0, 0]) <= bound[0, 0] + half_ulp(O[0, 0], "bf16") + 1e-6), (b, h)
+        assert np.all(np.abs(lse[b, h].cpu().numpy() - lse_ref[0, 0]) <= lb[0, 0] + 1e-5), (b, h)
+    z = _zero_heads(B, H)
+    assert (o.abs().amax(dim=(2, 3))[z] == 0).all(), "fp8: a zero head has O != 0"
+    lerr = (lse - math.log(N)).abs().amax(dim=2)
+    assert (lerr[z] <= 1e-5).all(), "fp8: a zero head has lse != ln N"
