@@ -34,8 +34,11 @@ METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak; HBM bytes vs Q/K/V/O mi
 _COMMON_SOURCES = ["exact_io_aware_73_amd/csrc/device_common.hpp", "exact_io_aware_73_amd/build.py"]
 KERNEL_SOURCES = {
     ("bf16", 64): ["exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows32.hip"],
+    # head dim 128 runs rows64 or rows32 by shape (the rule is in kernels.hpp)
     ("bf16", 128): ["exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows64.hip",
-                    "exact_io_aware_73_amd/csrc/rows64_pipeline.hpp"],
+                    "exact_io_aware_73_amd/csrc/rows64_pipeline.hpp",
+                    "exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows32.hip",
+                    "exact_io_aware_73_amd/csrc/kernels.hpp"],
     ("f32", 64): ["exact_io_aware_73_amd/csrc/attn_fwd_f32.hip"],
     ("f32", 128): ["exact_io_aware_73_amd/csrc/attn_fwd_f32.hip"],
 }

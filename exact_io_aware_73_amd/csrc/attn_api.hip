@@ -15,6 +15,7 @@ namespace {
 
 // MI355X (gfx950): 8 XCDs, workgroups dispatched round-robin over them.
 constexpr int kXcds = 8;
+constexpr int kCus = 256;   // MI355X compute units (steers only the d = 128 kernel choice)
 // A launch's work-items must stay below 2^32; every kernel here uses 256.
 constexpr uint64_t kMaxWorkgroups = (1ull << 32) / 256 - 1;
 
@@ -92,7 +93,7 @@ int fwd_impl(bool bf16, const void* q, const void* k, const void* v, void* o, fl
              int Hq, int Hkv, int N, int d, float scale, void* stream) {
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
   if (st != ATTN_OK) return st;
-  const bool rows64 = attn::fwd_bf16_use_rows64(d);
+  const bool rows64 = attn::fwd_bf16_use_rows64(B, Hq, Hkv, N, d, kCus);
   const uint64_t grid = !bf16 ? attn::fwd_f32_grid(B, Hq, N)
                       : rows64 ? attn::fwd_bf16_rows64_grid(B, Hq, Hkv, N)
                                : attn::fwd_bf16_rows32_grid(B, Hq, Hkv, N);

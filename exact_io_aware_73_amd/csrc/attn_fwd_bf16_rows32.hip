@@ -1,5 +1,6 @@
 // attn_fwd_bf16_rows32.hip -- fused, tiled attention forward for gfx950,
-// bf16 I/O, one 32-row query block per wave (used for head dim 64).
+// bf16 I/O, one 32-row query block per wave (head dim 64; head dim 128 where
+// the keys are short or the grid is small, as chosen in kernels.hpp).
 //
 // The IO-aware forward (blog "attention 的显存线性化", section 三; the
 // "efficient attention" chapter's online-softmax paragraph): one workgroup
@@ -12,7 +13,8 @@
 //    32 KB of LDS, so four workgroups (four waves per SIMD) share a CU: at
 //    d = 64 the softmax has as many vector instructions per MFMA as at
 //    d = 128 has per two, and the other waves' instructions fill the gaps
-//    one wave leaves while it waits on its own dependencies.
+//    one wave leaves while it waits on its own dependencies.  At head dim
+//    128 (214 VGPRs, 64 KB of LDS) two workgroups share a CU.
 //  * Each wave computes S^T = K Q^T per 32-key
 //    block with v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the
 //    wave's Q rows resident in VGPRs as the B operand).  In that output
@@ -442,7 +444,7 @@ uint64_t fwd_bf16_rows32_grid(int B, int Hq, int Hkv, int N) {
 }
 
 hipError_t launch_fwd_bf16_rows32(const FwdArgs& a) {
-  // head dim 64 only (head dim 128 runs the rows64 kernel)
+  if (a.d == 128) return a.scale < 0.0f ? launch_d<128, true>(a) : launch_d<128, false>(a);
   if (a.d != 64) return hipErrorInvalidValue;
   return a.scale < 0.0f ? launch_d<64, true>(a) : launch_d<64, false>(a);
 }

@@ -1,5 +1,6 @@
-// attn_fwd_bf16_rows64.hip -- the attn_fwd kernel for head dim 128 (and the
-// d = 64 instantiation): every key of a head per workgroup.  The kernel body
+// attn_fwd_bf16_rows64.hip -- the attn_fwd kernel for head dim 128 on long
+// keys with a grid that fills the GPU (and the d = 64 instantiation): every
+// key of a head per workgroup.  The kernel body
 // and its design notes are in rows64_pipeline.hpp.
 #define ATTN_ROWS64_SPLIT 0
 #include "rows64_pipeline.hpp"

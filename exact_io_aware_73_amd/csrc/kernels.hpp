@@ -36,14 +36,22 @@ uint64_t fwd_bf16_rows64_grid(int B, int Hq, int Hkv, int N);
 uint64_t fwd_f32_grid(int B, int Hq, int N);
 
 // Fused bf16 forward, two kernel designs:
-//   rows32 -- one 32-row query block per wave, four workgroups per CU
-//             (head dim 64 only: the softmax, not LDS, bounds it there);
+//   rows32 -- one 32-row query block per wave, 128 query rows per
+//             workgroup; four workgroups per CU at head dim 64, two at 128;
 //   rows64 -- two 32-row query blocks per wave sharing every K / V fragment
-//             read from LDS, software-pipelined across key tiles (head dim
-//             128, where LDS bandwidth bounds the one-block layout).
+//             read from LDS, software-pipelined across key tiles, 256 query
+//             rows per workgroup, one workgroup per CU (head dim 128).
+// Head dim 128 takes rows64 where the keys are long (N >= 8192) and its grid
+// has at least one workgroup per CU; elsewhere rows32, whose smaller
+// workgroups spread a small grid over every CU and hide the per-workgroup
+// start and end behind a second workgroup (measured: N = 200 GQA +24 %,
+// one head of 32768 rows +39 %, N = 4096 +2 %; N >= 8192 with a full grid
+// -2 ... -4 %).
 hipError_t launch_fwd_bf16_rows32(const FwdArgs& a);
 hipError_t launch_fwd_bf16_rows64(const FwdArgs& a);
-inline bool fwd_bf16_use_rows64(int d) { return d == 128; }
+inline bool fwd_bf16_use_rows64(int B, int Hq, int Hkv, int N, int d, int n_cu) {
+  return d == 128 && N >= 8192 && fwd_bf16_rows64_grid(B, Hq, Hkv, N) >= (uint64_t)n_cu;
+}
 hipError_t launch_fwd_f32(const FwdArgs& a);
 
 // 8-bit (OCP E4M3) forward on the FP8 MFMA; V^T rows of Np = fp8_padded_keys(N) bytes.

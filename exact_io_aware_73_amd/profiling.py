@@ -3,7 +3,7 @@
     python -m exact_io_aware_73_amd.profiling stats  <trace_kernel_stats.csv> <out.txt> "<command>"
         [<trace_kernel_trace.csv> <last_k>]
     python -m exact_io_aware_73_amd.profiling counters <workload> <fetch.csv> <write.csv>
-        <copy_fetch.csv> <copy_write.csv> <copy_mib> <out.json> "<commands>"
+        <copy_fetch.csv> <copy_write.csv> <copy_mib> <out.json> "<commands>" <kernel_source_sha>
 
 ``stats`` turns a ``--kernel-trace --stats`` CSV into a short text table;
 given the per-dispatch trace and K, it adds each kernel's mean over its

@@ -360,6 +360,19 @@ def check_sampled(q, k, v, o, lse, scale, dtype, seed=0):
     return worst
 
 
+@pytest.mark.parametrize("scale", [1 / math.sqrt(128), -0.05])
+def test_rows64_long_ragged(attn, scale):
+    """Head dim 128 with N >= 8192 and a grid of at least one workgroup per CU
+    runs the rows64 kernel (shorter keys or smaller grids run rows32): a
+    ragged last key tile and a GQA group, sampled rows against the oracle."""
+    B, Hq, Hkv, N, d = 1, 16, 4, 8197, 128
+    _say(f"[parity] rows64 long ragged {B},{Hq},{Hkv},{N},{d} scale={scale}")
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=8197)
+    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), scale)
+    torch.cuda.synchronize()
+    check_sampled(q, k, v, o.cpu(), lse.cpu(), scale, "bf16", seed=5)
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_workload(attn, name):
     w = workloads.WORKLOADS[name]
