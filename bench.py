@@ -55,26 +55,69 @@ def kernel_source_hash(workload: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str, per_launch_flops: int, profiles_dir: str | None = None):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this workload, or None when absent or taken on other kernel source."""
-    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"),
-                        f"attn_fwd_{workload}_counters.json")
+# the sources of the three kernels of the materialising path
+MATERIALIZED_SOURCES = ["exact_io_aware_73_amd/csrc/attn_materialized.hip",
+                        "exact_io_aware_73_amd/csrc/bf16_tiles.hpp"]
+
+
+def materialized_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in MATERIALIZED_SOURCES + _COMMON_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counters(path: str, sha: str):
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != kernel_source_hash(workload):
+    if rec.get("kernel_source_sha") != sha:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
-def time_launches(fn, stream, steps: int, warmup: int):
+def traffic_from_profiles(workload: str, per_launch_flops: int = 0, profiles_dir: str | None = None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, or None when absent or taken on other kernel source."""
+    rec = _counters(os.path.join(profiles_dir or os.path.join(ROOT, "profiles"),
+                                 f"attn_fwd_{workload}_counters.json"), kernel_source_hash(workload))
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def materialized_traffic_from_profiles(workload: str, profiles_dir: str | None = None):
+    """(read, write) bytes per call of the materialising path (its three
+    kernels summed) from the committed counter summary, or None."""
+    rec = _counters(os.path.join(profiles_dir or os.path.join(ROOT, "profiles"),
+                                 f"attn_fwd_materialized_{workload}_counters.json"),
+                    materialized_source_hash())
+    if rec is None:
+        return None
+    return rec["hbm_read_bytes_per_launch"], rec["hbm_write_bytes_per_launch"]
+
+
+def warm_up(fn, warmup: int, min_ms: float):
+    """`warmup` launches, then more until at least `min_ms` of wall time has
+    been spent launching: the GPU runs its first tens of milliseconds of work
+    at a lower clock, so a count of launches alone does not warm it at short
+    workloads.  Returns (launches run, wall ms)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        n += 1
+        if n >= warmup and n % 4 == 0:
+            torch.cuda.synchronize()   # let the wall clock see the work, not the enqueue
+    torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+def time_launches(fn, stream, steps: int, warmup: int, min_warm_ms: float = 0.0):
     """Wall time of `steps` launches (synchronised on both sides) and the
     mean per-launch duration from HIP events recorded on `stream`."""
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn, warmup, min_warm_ms)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -89,36 +132,69 @@ def time_launches(fn, stream, steps: int, warmup: int):
     return wall / steps * 1e3, float(np.mean(ev)), float(np.min(ev)), float(np.median(ev))
 
 
-def cpu_baseline(w, q, k, v, scale, budget_s: float = 12.0):
-    """The fp64 oracle, as it stands, on the host cores: whole (b, h) heads
-    of the same inputs until the time budget is spent (passing over the
-    workload again when it finishes sooner, so the rate is not taken from a
-    run of a second or two)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, q, k, v, scale, budget_s: float = 12.0, threads: int = 16):
+    """The fp64 oracle, as it stands, on the host cores, over a bounded sample
+    of the same inputs: units of whole query rows of one head (all of a
+    head's rows when a head is small, blocks of rows of ~1 GFLOP when it is
+    long), handed in order to a pool of `threads` workers (single-threaded
+    BLAS each) until the time budget is spent, passing over the workload
+    again when it finishes sooner.  The rate counts the units completed."""
     import oracle
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    from threadpoolctl import threadpool_limits
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
     B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
-    heads = [(b, h) for b in range(B) for h in range(Hq)]
-    g = Hq // Hkv
-    batch = -(-max(cores, 1) // g) * g    # whole K/V groups per batch
-    done = 0
+    rows = max(1, min(N, (1 << 30) // (4 * N * d)))
+    units = [(b, h, r0, min(N, r0 + rows)) for b in range(B) for h in range(Hq)
+             for r0 in range(0, N, rows)]
+    import functools
+    import threading
+    lock = threading.Lock()
+
+    @functools.lru_cache(maxsize=2 * threads)
+    def kv64(b, kv):   # a K/V head as float64, shared by the units that read it
+        return workloads.to_f64(k[b, kv]), workloads.to_f64(v[b, kv])
+
+    def run(u):
+        b, h, r0, r1 = u
+        with lock:
+            kk, vv = kv64(b, oracle.kv_head(h, Hq, Hkv))
+        oracle.attention_head(workloads.to_f64(q[b, h, r0:r1]), kk, vv, scale)
+        return r1 - r0
+
+    done_rows = 0
+    n_units = 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        start = done % len(heads)
-        sel = heads[start:start + batch]
-        for b in sorted({b for b, _ in sel}):
-            hs = [h for bb, h in sel if bb == b]
-            h0, h1 = min(hs), max(hs) + 1          # a whole number of groups
-            qq = workloads.to_f64(q[b:b + 1, h0:h1])
-            kk = workloads.to_f64(k[b:b + 1, h0 // g:h1 // g])
-            vv = workloads.to_f64(v[b:b + 1, h0 // g:h1 // g])
-            oracle.attention_ref(qq, kk, vv, scale, workers=cores)
-        done += len(sel)
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(threads) as ex:
+        pending = set()
+        i = 0
+        while True:
+            while len(pending) < threads and time.perf_counter() - t0 < budget_s:
+                pending.add(ex.submit(run, units[i % len(units)]))
+                i += 1
+            if not pending:
+                break
+            fin, pending = wait(pending, return_when=FIRST_COMPLETED)
+            for fu in fin:
+                done_rows += fu.result()
+                n_units += 1
     t = time.perf_counter() - t0
-    flops = acc.attn_fwd_flops(1, done, N, d)
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{done} (b, h) heads ({done / len(heads):.2f} passes over the {len(heads)}) "
-                       f"of {w.name}, fp64 NumPy, {t:.1f} s"),
-            "seconds": round(t, 3)}
+    flops = 4 * done_rows * N * d
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{n_units} units of up to {rows} query rows x all {N} keys "
+                       f"({done_rows / (B * Hq * N):.3f} of the workload's rows) of {w.name}, "
+                       f"fp64 NumPy, {threads} worker threads, {t:.1f} s"),
+            "seconds": round(t, 3), "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
 
 
 def mfma_ceiling(step_zero, stream, flops, steps: int):
@@ -153,6 +229,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-threads", type=int, default=min(len(os.sched_getaffinity(0)), 16),
+                    help="worker threads of the CPU oracle baseline")
+    ap.add_argument("--min-warmup-ms", type=float, default=200.0,
+                    help="keep launching warm-up steps until this much wall time has passed "
+                         "(the clock settles over the first tens of milliseconds of work)")
     ap.add_argument("--split", type=int, default=0,
                     help="time the split-KV entry point (attn_fwd_split) with this many key "
                          "ranges instead of attn_fwd (bf16 only)")
@@ -219,7 +300,15 @@ def main():
         entry(qd, kd, vd, o, lse, scale, stream)
 
     with torch.cuda.stream(stream):
-        ms_step, ev_mean, ev_min, ev_med = time_launches(step, stream, args.steps, args.warmup)
+        n_warm, warm_ms = warm_up(step, args.warmup, args.min_warmup_ms)
+        ms_step, ev_mean, ev_min, ev_med = time_launches(step, stream, args.steps, 0)
+    n_cu, n_xcd = attn.attn_device_info()
+    kernel = ("attn_fwd_f32_kernel" if w.dtype != "bf16" else
+              "attn_fwd_fp8_kernel" if fp8 else
+              "attn_fwd_bf16_rows64_split_kernel + attn_split_merge_kernel" if args.split else
+              {attn.ATTN_KERNEL_ROWS32: "attn_fwd_bf16_rows32_kernel",
+               attn.ATTN_KERNEL_ROWS64: "attn_fwd_bf16_rows64_kernel"}[
+                   attn.attn_fwd_plan(w.B, w.Hq, w.Hkv, w.N, w.d)] + f"<{w.d}>")
 
     flops = acc.attn_fwd_flops(w.B, w.Hq, w.N, w.d)
     minb = acc.min_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.elem_bytes)
@@ -231,14 +320,23 @@ def main():
     traffic = None if (args.split or fp8) else traffic_from_profiles(w.name, flops)
     roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic, "kernel_ms_mean": round(ev_mean, 4),
+                "traffic": traffic, "kernel": kernel, "kernel_ms_mean": round(ev_mean, 4),
                 "kernel_ms_min": round(ev_min, 4), "kernel_ms_median": round(ev_med, 4),
                 "min_bytes": minb,
-                "traffic_vs_min": (round(traffic / minb, 3) if traffic else None)}
+                "traffic_vs_min": (round(traffic / minb, 3) if traffic else None),
+                # achieved HBM bandwidth: the counted bytes over the mean kernel time
+                "hbm_gbps": (round(traffic / (ev_mean * 1e-3) / 1e9, 1) if traffic else None),
+                "hbm_frac": (round(traffic / (ev_mean * 1e-3) / 1e9 / acc.PEAK_HBM_GBPS, 4)
+                             if traffic else None),
+                "device": {"compute_units": n_cu, "xcds": n_xcd}}
 
     materialized = None
-    if (not args.no_materialized and not fp8
-            and w.B * w.Hq * w.N * w.N * (4 + w.elem_bytes) < (64 << 30)):
+    sp_bytes = w.B * w.Hq * w.N * w.N * (4 + w.elem_bytes)
+    if not w.materialized and not args.no_materialized and not fp8:
+        materialized = {"skipped": f"S and P would take {sp_bytes / 1e9:.1f} GB; this workload "
+                                   "runs only the tiled path (long_b4_h32_n4096_d128 and "
+                                   "gpt2_medium_b64_h16_n1024_d64 carry the comparison)"}
+    elif not args.no_materialized and not fp8 and sp_bytes < (64 << 30):
         s = torch.empty((w.B, w.Hq, w.N, w.N), dtype=torch.float32, device="cuda")
         p = torch.empty((w.B, w.Hq, w.N, w.N), dtype=w.torch_dtype, device="cuda")
         o2 = torch.empty_like(qd)
@@ -251,8 +349,17 @@ def main():
         with torch.cuda.stream(stream):
             m_ms, m_ev, _, _ = time_launches(mstep, stream, max(3, args.steps // 5), 2)
         pred = acc.materialized_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.elem_bytes)
+        meas = materialized_traffic_from_profiles(w.name)
+        mbytes = sum(meas) if meas else None
         materialized = {"ms": round(m_ev, 4), "tflops": round(flops / (m_ev * 1e-3) / 1e12, 2),
                         "predicted_bytes": pred, "predicted_vs_min": round(pred / minb, 2),
+                        "measured_bytes": mbytes,
+                        "measured_read_write": list(meas) if meas else None,
+                        "measured_vs_predicted": round(mbytes / pred, 3) if mbytes else None,
+                        "measured_vs_min": round(mbytes / minb, 2) if mbytes else None,
+                        "hbm_gbps": round(mbytes / (m_ev * 1e-3) / 1e9, 1) if mbytes else None,
+                        "hbm_frac": (round(mbytes / (m_ev * 1e-3) / 1e9 / acc.PEAK_HBM_GBPS, 4)
+                                     if mbytes else None),
                         "speedup_fused": round(m_ev / ev_mean, 2)}
         del s, p
 
@@ -292,11 +399,12 @@ def main():
             import oracle
             q, k, v = (torch.from_numpy(x) for x in oracle.dequantize(
                 fp8[0].numpy(), fp8[1].numpy(), fp8[2].numpy(), *fp8[3:], w.N))
-        cpu = cpu_baseline(w, q, k, v, scale, args.cpu_budget)
+        cpu = cpu_baseline(w, q, k, v, scale, args.cpu_budget, args.cpu_threads)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "warmup_run": {"launches": n_warm, "ms": round(warm_ms, 1)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3" if fp8 else ("bf16" if w.dtype == "bf16" else "f32"),
         "data": "synthetic",

@@ -78,7 +78,10 @@ PEAK_CLOCK_GHZ = 2.4
 BF16_DENSE_FLOP_PER_CLK_PER_CU = 4096
 PEAK_BF16_TFLOPS = 2516.6          # 256 CU * 2.4 GHz * 4096 FLOP/clk
 PEAK_FP8_TFLOPS = 5033.2           # dense FP8 MFMA: twice the bf16 rate
-PEAK_FP32_VECTOR_TFLOPS = 157.3    # packed fp32 FMA
+# fp32 vector FMA without the packed (two-per-lane) instructions, which the
+# library is built without: 256 CU * 2.4 GHz * 64 FMA lanes * 2 FLOP.  The
+# published 157.3 TFLOP/s counts the packed form.
+PEAK_FP32_VECTOR_TFLOPS = 78.6
 PEAK_HBM_GBPS = 8000.0
 
 

@@ -14,6 +14,9 @@ Entry points carry the C names and take tensors instead of raw pointers:
     attn_fwd_split_workspace_bytes(B, Hq, N, d, n_split)
     attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, stream=None)   bf16
     attn_bwd_workspace_bytes(B, Hq, N)
+    attn_fwd_fp8(q8, k8, vt8, o, lse, q_scale, k_scale, v_scale, scale, stream=None)
+    attn_device_info(device=None) -> (compute units, XCDs)
+    attn_fwd_plan(B, Hq, Hkv, N, d, device=None) -> ATTN_KERNEL_ROWS32 / _ROWS64
     attn_strerror(status)
 
 plus ``fwd`` / ``fwd_materialized`` / ``fwd_split`` / ``bwd``, which allocate
@@ -60,10 +63,16 @@ _lib.attn_fwd_fp8.restype = _I
 _lib.attn_strerror.argtypes = [_I]
 _lib.attn_strerror.restype = ctypes.c_char_p
 
+_lib.attn_device_info.argtypes = [ctypes.POINTER(_I), ctypes.POINTER(_I)]
+_lib.attn_device_info.restype = _I
+_lib.attn_fwd_plan.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_I)]
+_lib.attn_fwd_plan.restype = _I
+
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_GQA, ATTN_ERR_HEADDIM = 0, 1, 2, 3, 4
-ATTN_ERR_SCALE, ATTN_ERR_ALIGN, ATTN_ERR_ALIAS, ATTN_ERR_HIP = 5, 6, 7, 8
+ATTN_ERR_SCALE, ATTN_ERR_ALIGN, ATTN_ERR_HIP, ATTN_ERR_ALIAS = 5, 6, 7, 8
 ATTN_ERR_SPLIT, ATTN_ERR_WORKSPACE = 9, 10
 ATTN_MAX_SPLIT = 64
+ATTN_KERNEL_ROWS32, ATTN_KERNEL_ROWS64 = 1, 2
 
 
 def attn_strerror(status: int) -> str:
@@ -245,6 +254,25 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, stream=None):
                            _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, Hq, Hkv, N, d,
                            ctypes.c_float(float(scale)), _stream_handle(stream, q.device))
     _raise(st, fn_name)
+
+
+def attn_device_info(device=None):
+    """(compute units, XCDs) of a device as the library reads them (C: attn_device_info)."""
+    cu, xcd = _I(0), _I(0)
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        st = _lib.attn_device_info(ctypes.byref(cu), ctypes.byref(xcd))
+    _raise(st, "attn_device_info")
+    return cu.value, xcd.value
+
+
+def attn_fwd_plan(B, Hq, Hkv, N, d, device=None) -> int:
+    """ATTN_KERNEL_ROWS32 or ATTN_KERNEL_ROWS64: the kernel attn_fwd launches for
+    these sizes on ``device`` (C: attn_fwd_plan)."""
+    kern = _I(0)
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        st = _lib.attn_fwd_plan(int(B), int(Hq), int(Hkv), int(N), int(d), ctypes.byref(kern))
+    _raise(st, "attn_fwd_plan")
+    return kern.value
 
 
 def _scale(scale, d):

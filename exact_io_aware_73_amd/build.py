@@ -3,7 +3,9 @@
     python -m exact_io_aware_73_amd.build
 
 Compiles every ``csrc/*.hip`` to an object under ``_build/`` (in parallel)
-and links ``libattn.so`` next to this file.  Always recompiles.
+and links ``libattn.so`` next to this file.  Always recompiles; objects
+under ``_build/`` whose source is gone are deleted first, so nothing stale
+sits beside the library.
 """
 from __future__ import annotations
 
@@ -53,6 +55,10 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not sources:
         raise RuntimeError(f"no HIP sources under {CSRC}")
+    wanted = {os.path.basename(src) + ".o" for src in sources}
+    for obj in glob.glob(os.path.join(BUILD, "*.o")):
+        if os.path.basename(obj) not in wanted:
+            os.remove(obj)
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")

@@ -8,16 +8,51 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "kernels.hpp"
 
 namespace {
 
-// MI355X (gfx950): 8 XCDs, workgroups dispatched round-robin over them.
-constexpr int kXcds = 8;
-constexpr int kCus = 256;   // MI355X compute units (steers only the d = 128 kernel choice)
 // A launch's work-items must stay below 2^32; every kernel here uses 256.
 constexpr uint64_t kMaxWorkgroups = (1ull << 32) / 256 - 1;
+
+// ---------------------------------------------------------------------------
+// Device facts, read once per device: the compute-unit count (the d = 128
+// forward picks rows32 or rows64 by it) and the XCD count (workgroups are
+// dealt round-robin over the XCDs, each with its own L2; the kernels remap
+// their ids by it so that the workgroups of one K/V head share an L2).  A
+// partitioned part reports its own counts.
+struct DeviceFacts {
+  int n_cu = 0;
+  int n_xcd = 1;
+  hipError_t err = hipSuccess;
+};
+constexpr int kMaxDevices = 64;
+std::once_flag g_facts_once[kMaxDevices];
+DeviceFacts g_facts[kMaxDevices];
+
+// Facts of the calling thread's current device; a HIP error otherwise.
+hipError_t device_facts(DeviceFacts* out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_facts_once[dev], [dev] {
+    DeviceFacts f;
+    int cu = 0, xcc = 0;
+    f.err = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (f.err == hipSuccess)
+      f.err = hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev);
+    if (f.err == hipSuccess && cu < 1) f.err = hipErrorInvalidDevice;
+    f.n_cu = cu;
+    f.n_xcd = xcc > 0 ? xcc : 1;
+    g_facts[dev] = f;
+  });
+  *out = g_facts[dev];
+  return out->err;
+}
 
 struct Range {
   uintptr_t lo, hi;   // [lo, hi)
@@ -67,7 +102,8 @@ int check_alias(const void* q, const void* k, const void* v, const void* o, cons
 }
 
 attn::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse, float* s,
-                        void* p, int B, int Hq, int Hkv, int N, int d, float scale, void* stream) {
+                        void* p, int B, int Hq, int Hkv, int N, int d, float scale, int n_xcd,
+                        void* stream) {
   attn::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -82,29 +118,41 @@ attn::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, fl
   a.N = N;
   a.d = d;
   a.scale = scale;
-  a.n_xcd = kXcds;
+  a.n_xcd = n_xcd;
   a.stream = static_cast<hipStream_t>(stream);
   return a;
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// Sizes the fused forward accepts (pointers aside).  rows32's grid (128 rows
+// per workgroup) is the larger of the two bf16 kernels', so it bounds both.
+int check_fwd_sizes(bool bf16, int B, int Hq, int Hkv, int N, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  const uint64_t grid = bf16 ? attn::fwd_bf16_rows32_grid(B, Hq, Hkv, N) : attn::fwd_f32_grid(B, Hq, N);
+  if (grid > kMaxWorkgroups) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
 int fwd_impl(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse, int B,
              int Hq, int Hkv, int N, int d, float scale, void* stream) {
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
   if (st != ATTN_OK) return st;
-  const bool rows64 = attn::fwd_bf16_use_rows64(B, Hq, Hkv, N, d, kCus);
-  const uint64_t grid = !bf16 ? attn::fwd_f32_grid(B, Hq, N)
-                      : rows64 ? attn::fwd_bf16_rows64_grid(B, Hq, Hkv, N)
-                               : attn::fwd_bf16_rows32_grid(B, Hq, Hkv, N);
-  if (grid > kMaxWorkgroups) return ATTN_ERR_SHAPE;
+  st = check_fwd_sizes(bf16, B, Hq, Hkv, N, d);
+  if (st != ATTN_OK) return st;
   const int elem = bf16 ? 2 : 4;
   st = check_alias(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, elem, 0);
   if (st != ATTN_OK) return st;
-  const attn::FwdArgs a = make_args(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, scale, stream);
-  return to_status(!bf16 ? attn::launch_fwd_f32(a)
-                   : rows64 ? attn::launch_fwd_bf16_rows64(a)
-                            : attn::launch_fwd_bf16_rows32(a));
+  DeviceFacts f;
+  if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
+  const attn::FwdArgs a =
+      make_args(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, scale, f.n_xcd, stream);
+  if (!bf16) return to_status(attn::launch_fwd_f32(a));
+  return to_status(attn::fwd_bf16_use_rows64(B, Hq, Hkv, N, d, f.n_cu)
+                       ? attn::launch_fwd_bf16_rows64(a)
+                       : attn::launch_fwd_bf16_rows32(a));
 }
 
 int materialized_impl(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -122,7 +170,9 @@ int materialized_impl(bool bf16, const void* q, const void* k, const void* v, vo
   const int elem = bf16 ? 2 : 4;
   st = check_alias(q, k, v, o, lse, s, p, B, Hq, Hkv, N, d, elem, elem);
   if (st != ATTN_OK) return st;
-  const attn::FwdArgs a = make_args(q, k, v, o, lse, s, p, B, Hq, Hkv, N, d, scale, stream);
+  DeviceFacts f;
+  if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
+  const attn::FwdArgs a = make_args(q, k, v, o, lse, s, p, B, Hq, Hkv, N, d, scale, f.n_xcd, stream);
   return to_status(bf16 ? attn::launch_materialized_bf16(a) : attn::launch_materialized_f32(a));
 }
 
@@ -158,7 +208,10 @@ int split_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     for (const Range& r : other)
       if (overlap(w, r)) return ATTN_ERR_ALIAS;
   }
-  attn::FwdArgs a = make_args(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, scale, stream);
+  DeviceFacts f;
+  if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
+  attn::FwdArgs a =
+      make_args(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, scale, f.n_xcd, stream);
   a.n_split = n_eff;
   a.chunk_keys = (int)chunk;
   a.part_o = static_cast<float*>(ws);
@@ -189,15 +242,18 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   const uint64_t qo = rows * d * 2, kv = (uint64_t)B * Hkv * N * d * 2;
   const Range in[6] = {rng(q, qo), rng(k, kv), rng(v, kv), rng(o, qo), rng(lse, rows * 4),
                        rng(dout, qo)};
+  const int n_out = 4;
   const Range out[4] = {rng(dq, qo), rng(dk, kv), rng(dv, kv), rng(ws, need)};
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < n_out; ++i) {
     for (const Range& r : in)
       if (overlap(out[i], r)) return ATTN_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = i + 1; j < n_out; ++j)
       if (overlap(out[i], out[j])) return ATTN_ERR_ALIAS;
   }
+  DeviceFacts f;
+  if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
   attn::FwdArgs a = make_args(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), nullptr,
-                              nullptr, B, Hq, Hkv, N, d, scale, stream);
+                              nullptr, B, Hq, Hkv, N, d, scale, f.n_xcd, stream);
   attn::BwdArgs g;
   g.dout = dout;
   g.dq = dq;
@@ -231,7 +287,10 @@ int fp8_impl(const void* q8, const void* k8, const void* vt8, void* o, float* ls
     for (const Range& r : in)
       if (overlap(out[i], r)) return ATTN_ERR_ALIAS;
   if (overlap(out[0], out[1])) return ATTN_ERR_ALIAS;
-  attn::FwdArgs a = make_args(q8, k8, vt8, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, c, stream);
+  DeviceFacts f;
+  if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
+  attn::FwdArgs a =
+      make_args(q8, k8, vt8, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, c, f.n_xcd, stream);
   a.v_scale = v_scale;
   return to_status(attn::launch_fwd_fp8(a));
 }
@@ -325,6 +384,33 @@ ATTN_API unsigned long long attn_bwd_workspace_bytes(int B, int Hq, int N) {
   return (uint64_t)B * Hq * (uint64_t)N * 4u;
 }
 
+ATTN_API int attn_device_info(int* n_cu, int* n_xcd) {
+  try {
+    DeviceFacts f;
+    if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
+    if (n_cu) *n_cu = f.n_cu;
+    if (n_xcd) *n_xcd = f.n_xcd;
+    return ATTN_OK;
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+ATTN_API int attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int* kernel) {
+  try {
+    if (!kernel) return ATTN_ERR_NULL;
+    const int st = check_fwd_sizes(true, B, Hq, Hkv, N, d);
+    if (st != ATTN_OK) return st;
+    DeviceFacts f;
+    if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
+    *kernel = attn::fwd_bf16_use_rows64(B, Hq, Hkv, N, d, f.n_cu) ? ATTN_KERNEL_ROWS64
+                                                                 : ATTN_KERNEL_ROWS32;
+    return ATTN_OK;
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
 ATTN_API const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";
@@ -335,7 +421,7 @@ ATTN_API const char* attn_strerror(int status) {
     case ATTN_ERR_SCALE: return "scale must be finite";
     case ATTN_ERR_ALIGN: return "q/k/v/o/s/p must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_ALIAS: return "an output buffer overlaps an input or another output";
-    case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case ATTN_ERR_HIP: return "the HIP runtime reported an error (launch or device query)";
     case ATTN_ERR_SPLIT: return "n_split must be in [1, ATTN_MAX_SPLIT]";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned or too small";
     default: return "unknown status";

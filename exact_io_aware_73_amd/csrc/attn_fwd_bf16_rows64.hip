@@ -1,7 +1,7 @@
 // attn_fwd_bf16_rows64.hip -- the attn_fwd kernel for head dim 128 on long
-// keys with a grid that fills the GPU (and the d = 64 instantiation): every
-// key of a head per workgroup.  The kernel body
-// and its design notes are in rows64_pipeline.hpp.
+// keys with a grid that fills the GPU: every key of a head per workgroup.
+// The kernel body and its design notes are in rows64_pipeline.hpp (whose
+// d = 64 form serves only the split-KV path).
 #define ATTN_ROWS64_SPLIT 0
 #include "rows64_pipeline.hpp"
 
@@ -27,9 +27,9 @@ uint64_t fwd_bf16_rows64_grid(int B, int Hq, int Hkv, int N) {
 }
 
 hipError_t launch_fwd_bf16_rows64(const FwdArgs& a) {
+  if (a.d != 128) return hipErrorInvalidValue;   // head dim 64 runs rows32
   const bool neg = a.scale < 0.0f;
-  if (a.d == 128) return neg ? launch_d<128, true>(a) : launch_d<128, false>(a);
-  return neg ? launch_d<64, true>(a) : launch_d<64, false>(a);
+  return neg ? launch_d<128, true>(a) : launch_d<128, false>(a);
 }
 
 }  // namespace attn

@@ -46,7 +46,8 @@ uint64_t fwd_f32_grid(int B, int Hq, int N);
 // workgroups spread a small grid over every CU and hide the per-workgroup
 // start and end behind a second workgroup (measured: N = 200 GQA +24 %,
 // one head of 32768 rows +39 %, N = 4096 +2 %; N >= 8192 with a full grid
-// -2 ... -4 %).
+// -2 ... -4 %).  n_cu is the device's compute-unit count (read from the HIP
+// runtime once per device).
 hipError_t launch_fwd_bf16_rows32(const FwdArgs& a);
 hipError_t launch_fwd_bf16_rows64(const FwdArgs& a);
 inline bool fwd_bf16_use_rows64(int B, int Hq, int Hkv, int N, int d, int n_cu) {

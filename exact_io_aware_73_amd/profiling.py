@@ -4,6 +4,7 @@
         [<trace_kernel_trace.csv> <last_k>]
     python -m exact_io_aware_73_amd.profiling counters <workload> <fetch.csv> <write.csv>
         <copy_fetch.csv> <copy_write.csv> <copy_mib> <out.json> "<commands>" <kernel_source_sha>
+        [<kernel>,<kernel>,...]
 
 ``stats`` turns a ``--kernel-trace --stats`` CSV into a short text table;
 given the per-dispatch trace and K, it adds each kernel's mean over its
@@ -11,7 +12,10 @@ last K dispatches (the timed steps of a bench run, after its warm-up).
 ``counters`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
 the fused kernel, and the same two counters read on a plain device copy of
 known size, into HBM bytes per launch: each counter (KiB per dispatch) is
-scaled by known copy bytes / the counter's reading on the copy.
+scaled by known copy bytes / the counter's reading on the copy.  Given a
+comma-separated list of kernel names (substrings), the bytes of one call
+are the sum over those kernels of each one's median dispatch (the
+materialising path runs three kernels per call).
 """
 from __future__ import annotations
 
@@ -66,25 +70,36 @@ def counter_kib(path: str, kernel_substr: str):
 
 
 def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib,
-                     commands, kernel_source_sha):
+                     commands, kernel_source_sha, kernels=(FUSED_KERNEL,)):
     copy_bytes = int(copy_mib) << 20
     cf = statistics.median(counter_kib(copy_fetch_csv, COPY_KERNEL))
     cw = statistics.median(counter_kib(copy_write_csv, COPY_KERNEL))
     f_scale = copy_bytes / (cf * 1024)
     w_scale = copy_bytes / (cw * 1024)
-    fk = counter_kib(fetch_csv, FUSED_KERNEL)
-    wk = counter_kib(write_csv, FUSED_KERNEL)
-    fetch = statistics.median(fk) * 1024 * f_scale
-    write = statistics.median(wk) * 1024 * w_scale
-    return {
-        "workload": workload, "kernel": FUSED_KERNEL,
-        "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+    fetch = write = 0.0
+    per_kernel = {}
+    for kern in kernels:
+        fk = counter_kib(fetch_csv, kern)
+        wk = counter_kib(write_csv, kern)
+        kf = statistics.median(fk) * 1024 * f_scale
+        kw = statistics.median(wk) * 1024 * w_scale
+        fetch += kf
+        write += kw
+        per_kernel[kern] = {"fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+                            "read_bytes": round(kf), "write_bytes": round(kw)}
+    rec = {"workload": workload, "kernel": ",".join(kernels)}
+    if len(kernels) == 1:
+        rec.update({k: v for k, v in per_kernel[kernels[0]].items() if k.endswith("dispatch")})
+    else:
+        rec["per_kernel"] = per_kernel
+    rec.update({
         "copy_probe_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
         "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
         "hbm_read_bytes_per_launch": round(fetch), "hbm_write_bytes_per_launch": round(write),
         "hbm_bytes_per_launch": round(fetch + write),
         "kernel_source_sha": kernel_source_sha, "commands": commands,
-    }
+    })
+    return rec
 
 
 def main(argv):
@@ -95,8 +110,9 @@ def main(argv):
             text += last_k_table(argv[4], int(argv[5]))
         open(out, "w").write(text)
     elif argv[0] == "counters":
-        _, wl, f, w, cf, cw, mib, out, cmds, sha = argv
-        rec = counters_summary(wl, f, w, cf, cw, int(mib), cmds, sha)
+        _, wl, f, w, cf, cw, mib, out, cmds, sha = argv[:10]
+        kernels = tuple(argv[10].split(",")) if len(argv) > 10 else (FUSED_KERNEL,)
+        rec = counters_summary(wl, f, w, cf, cw, int(mib), cmds, sha, kernels)
         json.dump(rec, open(out, "w"), indent=1)
         print(json.dumps({k: rec[k] for k in ("workload", "hbm_read_bytes_per_launch",
                                                "hbm_write_bytes_per_launch")}))

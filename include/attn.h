@@ -27,16 +27,22 @@
  *
  * Pointers: every array pointer is a DEVICE pointer, allocated and owned by
  * the caller.  The library allocates no device memory and keeps no state
- * between calls other than immutable device facts.  Outputs (o, lse, s, p)
- * must not overlap the inputs or each other.
+ * between calls other than immutable device facts: the compute-unit and
+ * XCD counts of each device, read from the HIP runtime once per device
+ * (thread-safe, on the first call that launches work there).  Outputs
+ * (o, lse, s, p) must not overlap the inputs or each other.
+ *
+ * Device: work runs on the calling thread's current HIP device, which must
+ * be the device that holds the pointers and owns `stream`.
  *
  * Stream: `stream` is a hipStream_t passed as void*; NULL means the null
  * stream.  Work is enqueued and the call returns without synchronising.
  *
  * Errors: every argument is checked before any HIP call; a failed check
- * returns its attn_status_t code and enqueues nothing.  A launch failure
- * reported by the HIP runtime returns ATTN_ERR_HIP.  No entry point prints,
- * aborts or lets an exception escape.  attn_strerror() names a code.
+ * returns its attn_status_t code and enqueues nothing.  An error reported by
+ * the HIP runtime (a launch, or the device query) returns ATTN_ERR_HIP.  No
+ * entry point prints, aborts or lets an exception escape.  attn_strerror()
+ * names a code.
  *
  * Sizes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128}.  Element
  * offsets are computed in 64 bits; B*Hkv*ceil((Hq/Hkv)*N/128) workgroups
@@ -64,8 +70,8 @@ typedef enum {
   ATTN_ERR_HEADDIM = 4,  /* d is not 64 or 128 */
   ATTN_ERR_SCALE = 5,    /* scale is NaN or infinite */
   ATTN_ERR_ALIGN = 6,    /* q/k/v/o/s/p not 16-byte aligned, or lse not 4-byte aligned */
-  ATTN_ERR_ALIAS = 7,    /* an output overlaps an input or another output */
-  ATTN_ERR_HIP = 8,      /* the HIP runtime reported an error at launch */
+  ATTN_ERR_HIP = 7,      /* the HIP runtime reported an error (a launch, or a device query) */
+  ATTN_ERR_ALIAS = 8,    /* an output overlaps an input or another output */
   ATTN_ERR_SPLIT = 9,    /* n_split outside [1, ATTN_MAX_SPLIT] */
   ATTN_ERR_WORKSPACE = 10 /* workspace NULL, misaligned or smaller than required */
 } attn_status_t;
@@ -217,6 +223,30 @@ ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o
 
 /* attn_bwd_workspace_bytes -- B * Hq * N * 4; 0 for B, Hq or N < 1. */
 ATTN_API unsigned long long attn_bwd_workspace_bytes(int B, int Hq, int N);
+
+/*
+ * attn_device_info -- the device facts the launches use, for the calling
+ * thread's current device: the number of compute units (the fused bf16
+ * forward picks its kernel by it) and of XCDs, the dies with their own L2
+ * cache over which workgroups are dealt round-robin (the launch order maps
+ * the workgroups of one K/V head onto one XCD by it).  Read from the HIP
+ * runtime once per device and cached.  n_cu / n_xcd: host pointers, either
+ * may be NULL.  ATTN_ERR_HIP when the runtime cannot report them.
+ */
+ATTN_API int attn_device_info(int* n_cu, int* n_xcd);
+
+/* Fused bf16 forward kernels (the value attn_fwd_plan writes). */
+#define ATTN_KERNEL_ROWS32 1  /* 128 query rows per workgroup, one 32-row block per wave */
+#define ATTN_KERNEL_ROWS64 2  /* 256 query rows per workgroup, two 32-row blocks per wave */
+
+/*
+ * attn_fwd_plan -- which kernel attn_fwd launches for these sizes on the
+ * calling thread's current device: ATTN_KERNEL_ROWS64 for head dim 128 with
+ * N >= 8192 and at least one 256-row workgroup per compute unit, else
+ * ATTN_KERNEL_ROWS32.  The same argument checks as attn_fwd (pointers
+ * aside); *kernel (host pointer, not NULL) is written only on ATTN_OK.
+ */
+ATTN_API int attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int* kernel);
 
 /* attn_strerror -- a static, NUL-terminated description of a status code. */
 ATTN_API const char* attn_strerror(int status);

@@ -39,11 +39,20 @@ The reading taken here, stated as the contract of the 8-bit entry point:
     the relative part: 2^-12 for the fp32 arithmetic (exp2, the sums), and
     2 * eps_s * max_j A_ij for the scores, A_ij = |scale| * sum_c |q_ic| |k_jc|:
     the matrix core sums the exact 8-bit products into fp32 with an error
-    the contract bounds by eps_s * A_ij, eps_s = 2^-14 (a score error
-    dS_j moves the normalised weight w_j by a factor within
-    exp(+-2 max_j |dS_j|)).  The same eps_s * max_j A_ij bounds the error of
-    lse (``fp8_lse_bound``).  The final rounding of O to bf16 is the
-    caller's to add.
+    the contract bounds by eps_s * A_ij (a score error dS_j moves the
+    normalised weight w_j by a factor within exp(+-2 max_j |dS_j|)).  The
+    same eps_s * max_j A_ij bounds the error of lse (``fp8_lse_bound``).
+    The final rounding of O to bf16 is the caller's to add.
+  * eps_s.  A product of two E4M3 values has at most 8 significant bits, so
+    every product is exact in fp32; only the d - 1 additions round.  Summed
+    in ANY order (any tree of pairwise additions), each addition rounded
+    once, even toward zero (relative error < 2^-23 each), the sum differs
+    from the exact one by at most (d - 1) 2^-23 sum_c |q_c k_c|: at d = 128
+    that is 127 * 2^-23 < 2^-16.  The matrix core's internal order and
+    rounding are not documented, so the contract takes four times that,
+    eps_s = 2^-14, for the steps around it (the fp32 multiply by the scale,
+    any wider internal partial sums rounded more than once).  The largest
+    error seen on the GPU was about 2^-17 of the same sum.
   * For a statistical check: with independent rounding errors of relative
     size <= u (mean square <= u^2 / 3), the mean square of O' - O is at most
     (u^2 / 3) * sum_j w_ij^2 v_jc^2 per element; ``fp8_mean_square_bound``.
@@ -57,7 +66,8 @@ from .attention import attention_ref, head_scores, kv_head, softmax_rows
 U_E4M3 = 2.0 ** -4          # relative rounding error bound of E4M3 (3 mantissa bits)
 E_ABS = 2.0 ** -16          # absolute weight error bound, relative to the row's largest
 FP32_SLACK = 2.0 ** -12     # fp32 arithmetic around the 8-bit products
-EPS_S = 2.0 ** -14          # score error allowed per unit of sum_c |q_c k_c| * |scale|
+EPS_S = 2.0 ** -14          # score error allowed per unit of sum_c |q_c k_c| * |scale|:
+                            # 4 x the any-order, toward-zero fp32 summation bound at d = 128
 
 
 def padded_keys(N: int) -> int:
@@ -107,16 +117,33 @@ def _heads(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
             yield b, h, W, v[b, kv], ds
 
 
+def _bound(W, v, ds):
+    """The per-element bound of rows with exact weights W [rows, N], the K/V
+    head's v [N, d] and score-error bounds ds [rows]."""
+    av = np.abs(v)
+    rel = U_E4M3 + FP32_SLACK + 2.0 * ds[:, None]
+    return rel * (W @ av) + E_ABS * W.max(axis=1, keepdims=True) * av.sum(axis=0, keepdims=True)
+
+
 def fp8_error_bound(q8, k8, vt8, q_scale, k_scale, v_scale, scale) -> np.ndarray:
     """Per-element bound on |O_path - O| (before the output's bf16 rounding)."""
     q8 = np.asarray(q8)
     out = np.zeros(q8.shape, dtype=np.float64)
     for b, h, W, v, ds in _heads(q8, k8, vt8, q_scale, k_scale, v_scale, scale):
-        av = np.abs(v)
-        rel = U_E4M3 + FP32_SLACK + 2.0 * ds[:, None]
-        out[b, h] = (rel * (W @ av)
-                     + E_ABS * W.max(axis=1, keepdims=True) * av.sum(axis=0, keepdims=True))
+        out[b, h] = _bound(W, v, ds)
     return out
+
+
+def fp8_bounds_rows(q, k, v, b: int, h: int, rows, scale):
+    """The same two bounds for selected query rows of one head, from the
+    dequantised q, k, v (``dequantize``): (per-element bound [rows, d],
+    lse bound [rows]).  For sampled checks of shapes too large for the
+    whole-tensor functions."""
+    kv = kv_head(h, q.shape[1], k.shape[1])
+    qr = np.asarray(q[b, h])[np.asarray(rows)]
+    W, _ = softmax_rows(head_scores(qr, k[b, kv], scale))
+    ds = EPS_S * abs(scale) * (np.abs(qr) @ np.abs(k[b, kv]).T).max(axis=1)
+    return _bound(W, v[b, kv], ds), ds
 
 
 def fp8_lse_bound(q8, k8, vt8, q_scale, k_scale, v_scale, scale) -> np.ndarray:

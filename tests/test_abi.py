@@ -41,6 +41,8 @@ def lib():
     l.attn_fwd_fp8.argtypes = [P, P, P, P, P, F, F, F, I, I, I, I, I, F, P]
     l.attn_strerror.argtypes = [I]
     l.attn_strerror.restype = ctypes.c_char_p
+    l.attn_fwd_plan.argtypes = [I, I, I, I, I, ctypes.POINTER(I)]
+    l.attn_fwd_plan.restype = I
     return l
 
 
@@ -48,7 +50,30 @@ def test_header_declares_the_entry_points():
     assert set(_declared()) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_materialized",
                                 "attn_fwd_materialized_f32", "attn_fwd_split",
                                 "attn_fwd_split_workspace_bytes", "attn_bwd",
-                                "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_strerror"}
+                                "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_device_info",
+                                "attn_fwd_plan", "attn_strerror"}
+
+
+def test_status_numbering_is_pinned():
+    """The status values are part of the ABI: 0 - 7 as the boundary was
+    specified (ATTN_ERR_HIP = 7), the three codes added with the alias check,
+    the split-KV and the workspace arguments after them.  The binding's
+    constants carry the same values."""
+    want = {"ATTN_OK": 0, "ATTN_ERR_NULL": 1, "ATTN_ERR_SHAPE": 2, "ATTN_ERR_GQA": 3,
+            "ATTN_ERR_HEADDIM": 4, "ATTN_ERR_SCALE": 5, "ATTN_ERR_ALIGN": 6, "ATTN_ERR_HIP": 7,
+            "ATTN_ERR_ALIAS": 8, "ATTN_ERR_SPLIT": 9, "ATTN_ERR_WORKSPACE": 10}
+    assert _status_codes() == want
+    src = open(os.path.join(ROOT, "exact_io_aware_73_amd", "attn.py")).read()
+    m = re.findall(r"^(ATTN_[\w, ]+?)\s*=\s*([\d, ]+)$", src, re.M)
+    got = {}
+    for names, vals in m:
+        for n, v in zip(names.split(","), vals.split(",")):
+            got[n.strip()] = int(v)
+    assert {k: got[k] for k in want} == want
+    kern = {m.group(1): int(m.group(2))
+            for m in re.finditer(r"#define (ATTN_KERNEL_\w+) (\d+)", open(HEADER).read())}
+    assert kern == {"ATTN_KERNEL_ROWS32": got["ATTN_KERNEL_ROWS32"],
+                    "ATTN_KERNEL_ROWS64": got["ATTN_KERNEL_ROWS64"]}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -113,6 +138,19 @@ def test_fwd_rejects(lib, fn, kw, code):
 ])
 def test_materialized_rejects(lib, fn, kw, code):
     assert _mat(lib, fn, **kw) == _status_codes()[code]
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 2, 1, 16, 64), "ATTN_ERR_SHAPE"), ((1, 2, 0, 16, 64), "ATTN_ERR_SHAPE"),
+    ((1, 2, 1, 0, 128), "ATTN_ERR_SHAPE"), ((1, 3, 2, 16, 64), "ATTN_ERR_GQA"),
+    ((1, 2, 1, 16, 96), "ATTN_ERR_HEADDIM"), ((1 << 20, 1 << 10, 1 << 10, 1 << 10, 64), "ATTN_ERR_SHAPE"),
+])
+def test_plan_rejects(lib, args, code):
+    """attn_fwd_plan checks its sizes as attn_fwd does, before any HIP call."""
+    out = ctypes.c_int(-1)
+    assert lib.attn_fwd_plan(*args, ctypes.byref(out)) == _status_codes()[code]
+    assert out.value == -1
+    assert lib.attn_fwd_plan(1, 2, 1, 16, 64, None) == _status_codes()["ATTN_ERR_NULL"]
 
 
 def test_python_binding_signatures_match_header():

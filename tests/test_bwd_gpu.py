@@ -104,3 +104,47 @@ def test_python_bwd_rejects(attn):
                       torch.empty_like(q), ws, 0.125)
     with pytest.raises(ValueError):
         attn.bwd(q.float(), q.float(), q.float(), o, lse, q)
+
+
+# ---------------------------------------------------------------------------
+# the shapes the backward is timed on, at full size: the whole batch runs on
+# the GPU; sampled heads are checked element by element against the oracle
+# (a K/V head's dK and dV against the sum over every query head of its group)
+TIMED = {
+    "gpt2_medium_b64_h16_n1024_d64": 3,
+    "long_b4_h32_n4096_d128": 2,
+    "gqa_b2_hq32_hkv8_n8192_d128": 1,
+}
+
+
+@pytest.mark.parametrize("name", list(TIMED))
+def test_bwd_timed_workload(attn, name):
+    w = workloads.WORKLOADS[name]
+    print(f"[bwd] full workload {name}", flush=True)
+    q, k, v = workloads.make_inputs(w)
+    do = workloads.random_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, torch.bfloat16, seed=w.seed + 9)[0]
+    scale = 1 / math.sqrt(w.d)
+    dq, dk, dv = (t.cpu() for t in _grads(attn, q, k, v, do, scale))
+    g = w.Hq // w.Hkv
+    rng = np.random.default_rng(w.seed)
+    groups = {(0, 0), (w.B - 1, w.Hkv - 1)}
+    while len(groups) < TIMED[name]:
+        groups.add((int(rng.integers(w.B)), int(rng.integers(w.Hkv))))
+    for (b, kvh) in sorted(groups)[:TIMED[name]]:
+        kk, vv = workloads.to_f64(k[b, kvh]), workloads.to_f64(v[b, kvh])
+        dk_ref = np.zeros_like(kk)
+        dv_ref = np.zeros_like(vv)
+        for h in range(kvh * g, (kvh + 1) * g):
+            gq, gk, gv = oracle.attention_bwd_head(workloads.to_f64(q[b, h]), kk, vv,
+                                                   workloads.to_f64(do[b, h]), scale)
+            dk_ref += gk
+            dv_ref += gv
+            err = float(np.max(np.abs(workloads.to_f64(dq[b, h]) - gq)))
+            tol = 1e-2 * float(np.max(np.abs(gq))) + 1e-4
+            assert err <= tol, (name, (b, h), "dq", err, tol)
+        for gname, got, ref in (("dk", dk[b, kvh], dk_ref), ("dv", dv[b, kvh], dv_ref)):
+            err = float(np.max(np.abs(workloads.to_f64(got) - ref)))
+            tol = 1e-2 * float(np.max(np.abs(ref))) + 1e-4
+            assert err <= tol, (name, (b, kvh), gname, err, tol)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()

@@ -22,7 +22,6 @@ import torch
 
 import oracle
 import workloads
-from oracle import fp8 as F8
 from tests.parity import half_ulp
 
 pytestmark = pytest.mark.gpu
@@ -143,11 +142,7 @@ def test_fp8_full_size_sampled(attn):
     for b, h in [(0, 0), (1, 17), (3, 31)]:
         rows = np.sort(rng.choice(N, 24, replace=False))
         O, lse_ref = oracle.attention_ref_rows(q, k, v, b, h, rows, scale)
-        W, _ = oracle.softmax_rows(oracle.head_scores(q[b, h, rows], k[b, h], scale))
-        ds = F8.EPS_S * scale * (np.abs(q[b, h, rows]) @ np.abs(k[b, h]).T).max(axis=1)
-        av = np.abs(v[b, h])
-        bound = ((F8.U_E4M3 + F8.FP32_SLACK + 2.0 * ds[:, None]) * (W @ av)
-                 + F8.E_ABS * W.max(axis=1, keepdims=True) * av.sum(axis=0, keepdims=True))
+        bound, ds = oracle.fp8_bounds_rows(q, k, v, b, h, rows, scale)
         err = np.abs(o[b, h, rows] - O)
         assert np.all(err <= bound + half_ulp(O, "bf16") + 1e-6), (b, h)
         assert np.all(np.abs(lse[b, h, rows] - lse_ref) <= ds + 1e-5), (b, h)

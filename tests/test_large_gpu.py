@@ -93,6 +93,41 @@ def test_fwd_past_2_31_elements(attn, d):
     _check_fwd(o, lse, small, scale, f"fwd d={d}")
 
 
+def test_rows64_past_2_31_elements(attn):
+    """The rows64 kernel (head dim 128, N >= 8192, a full grid) on tensors
+    past 2^31 elements: 2 x 1025 heads of 8192 rows, the first and last
+    random and checked on sampled rows, every other head zero."""
+    B, H, Nl, d = 2, 1025, 8192, 128
+    assert B * H * Nl * d > MIN_ELEMENTS
+    assert attn.attn_fwd_plan(B, H, H, Nl, d) == attn.ATTN_KERNEL_ROWS64
+    _say(f"[large] attn_fwd rows64 B={B} H={H} N={Nl} d={d}")
+    small = workloads.random_inputs(1, 2, 2, Nl, d, torch.bfloat16, seed=1300)
+    big = []
+    for t in small:
+        g = torch.zeros((B, H, Nl, d), dtype=torch.bfloat16, device=DEVICE)
+        g[0, 0].copy_(t[0, 0])
+        g[B - 1, H - 1].copy_(t[0, 1])
+        big.append(g)
+    scale = 1 / math.sqrt(d)
+    o, lse = attn.fwd(*big, scale)
+    torch.cuda.synchronize()
+    del big
+    q, k, v = small
+    rng = np.random.default_rng(3)
+    rows = sorted(set(range(16)) | set(range(Nl - 16, Nl)) |
+                  set(rng.choice(Nl, size=32, replace=False).tolist()))
+    for i, (b, h) in enumerate([(0, 0), (B - 1, H - 1)]):
+        O_ref, l_ref = oracle.attention_head(workloads.to_f64(q[0, i]), workloads.to_f64(k[0, i]),
+                                             workloads.to_f64(v[0, i]), scale, rows=rows)
+        r = compare(workloads.to_f64(o[b, h, rows].cpu()), lse[b, h, rows].cpu().numpy(), O_ref,
+                    l_ref, "bf16")
+        assert r["ok"], ((b, h), r)
+    z = _zero_heads(B, H)
+    assert (o.abs().amax(dim=(2, 3))[z] == 0).all(), "rows64: a zero head has O != 0"
+    lerr = (lse - math.log(Nl)).abs().amax(dim=2)
+    assert (lerr[z] <= 1e-5).all(), "rows64: a zero head has lse != ln N"
+
+
 def test_split_past_2_31_elements(attn):
     B, H = SHAPES[128]
     _say(f"[large] attn_fwd_split B={B} H={H} N={N} d=128 n_split=2")

@@ -214,3 +214,69 @@ def test_mean_square_bound_holds_under_emulation():
     pred = (F.U_E4M3 ** 2 / 3.0) * ((W * W) @ (V * V))
     err = _emulate(S, V, rng) - O
     assert np.mean(err ** 2) <= np.mean(pred)
+
+
+def _f32_toward_zero(x):
+    """Round float64 values to float32 toward zero (a directed rounding)."""
+    r = x.astype(np.float32)
+    over = np.abs(r.astype(np.float64)) > np.abs(x)
+    r[over] = np.nextafter(r[over], np.float32(0.0))
+    return r
+
+
+def _sum_f32(prod, order, toward_zero):
+    """Sum the rows of `prod` (exact products) in fp32 in the given order:
+    'forward', 'reverse' (sequential) or 'tree' (pairwise), each addition
+    rounded once, to nearest or toward zero."""
+    rnd = _f32_toward_zero if toward_zero else (lambda x: x.astype(np.float32))
+    p = prod[:, ::-1] if order == "reverse" else prod
+    if order == "tree":
+        cur = p.astype(np.float32)
+        while cur.shape[1] > 1:
+            cur = rnd(cur[:, 0::2].astype(np.float64) + cur[:, 1::2].astype(np.float64))
+        return cur[:, 0].astype(np.float64)
+    acc = p[:, 0].astype(np.float32)
+    for c in range(1, p.shape[1]):
+        acc = rnd(acc.astype(np.float64) + p[:, c])
+    return acc.astype(np.float64)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_score_error_constant_covers_fp32_summation(d):
+    """Size of eps_s: E4M3 x E4M3 products are exact in fp32 (at most 8
+    significant bits); summing d of them in fp32 -- sequentially either way
+    or as a pairwise tree, rounding to nearest or toward zero -- stays within
+    (d - 1) 2^-23 sum_c |q_c k_c|, and eps_s is four times that bound at
+    d = 128.  Inputs span the E4M3 range, with mixed signs so the sums cancel."""
+    rng = np.random.default_rng(d)
+    codes = rng.integers(0, 256, size=(2, 4000, d)).astype(np.uint8)
+    vals = F.e4m3_decode(codes)
+    vals = np.where(np.isnan(vals), 0.0, vals)
+    prod = vals[0] * vals[1]
+    assert np.all(prod.astype(np.float32).astype(np.float64) == prod)   # exact in fp32
+    exact = prod.sum(axis=1)                                             # exact in fp64 here
+    mag = np.abs(prod).sum(axis=1)
+    bound = (d - 1) * 2.0 ** -23 * mag
+    worst = 0.0
+    for order in ("forward", "reverse", "tree"):
+        for tz in (False, True):
+            err = np.abs(_sum_f32(prod, order, tz) - exact)
+            assert np.all(err <= bound), (order, tz)
+            worst = max(worst, float(np.max(err / np.maximum(mag, 1e-300))))
+    assert worst > 0.0
+    assert F.EPS_S == 4 * 2.0 ** -16 and 127 * 2.0 ** -23 < 2.0 ** -16
+
+
+def test_bounds_rows_equal_the_whole_tensor_bounds():
+    """fp8_bounds_rows on selected rows of one head equals the rows of the
+    whole-tensor fp8_error_bound and fp8_lse_bound."""
+    q8, k8, vt8 = _random_fp8(2, 4, 2, 70, 64, 13)
+    args = (q8, k8, vt8, 0.6, 1.3, 0.4, 0.11)
+    b = F.fp8_error_bound(*args)
+    lb = F.fp8_lse_bound(*args)
+    q, k, v = F.dequantize(q8, k8, vt8, 0.6, 1.3, 0.4, 70)
+    rows = [0, 5, 33, 69]
+    for (bb, h) in [(0, 0), (1, 3), (0, 2)]:
+        got, ds = F.fp8_bounds_rows(q, k, v, bb, h, rows, 0.11)
+        np.testing.assert_allclose(got, b[bb, h, rows], rtol=1e-12)
+        np.testing.assert_allclose(ds, lb[bb, h, rows], rtol=1e-12)

@@ -360,17 +360,92 @@ def check_sampled(q, k, v, o, lse, scale, dtype, seed=0):
     return worst
 
 
+def check_every_head(q, k, v, o, lse, scale, dtype, seed=0, n_rows=4):
+    """Oracle on a few random rows of EVERY head."""
+    B, Hq, N, d = q.shape
+    rng = np.random.default_rng(seed + 1)
+    for b in range(B):
+        for kv in range(k.shape[1]):
+            kk, vv = workloads.to_f64(k[b, kv]), workloads.to_f64(v[b, kv])
+            g = Hq // k.shape[1]
+            for h in range(kv * g, (kv + 1) * g):
+                rows = sorted(rng.choice(N, size=min(n_rows, N), replace=False).tolist())
+                O_ref, l_ref = oracle.attention_head(workloads.to_f64(q[b, h, rows]), kk, vv, scale)
+                r = compare(workloads.to_f64(o[b, h, rows]), lse[b, h, rows].numpy(), O_ref, l_ref,
+                            dtype)
+                assert r["ok"], ((b, h), rows, r)
+
+
+def _rows64_plan(attn, B, Hq, Hkv, N, d):
+    kern = attn.attn_fwd_plan(B, Hq, Hkv, N, d)
+    assert kern == attn.ATTN_KERNEL_ROWS64, (B, Hq, Hkv, N, d, kern)
+
+
+def test_kernel_plan_by_shape(attn):
+    """Which kernel each bf16 shape runs, asked of the library: rows64 where
+    N >= 8192 and the 256-row grid has a workgroup per compute unit."""
+    n_cu, n_xcd = attn.attn_device_info()
+    _say(f"[parity] device: {n_cu} compute units, {n_xcd} XCDs")
+    assert n_cu >= 1 and n_xcd >= 1
+    R32, R64 = attn.ATTN_KERNEL_ROWS32, attn.ATTN_KERNEL_ROWS64
+    want = {"gpt2_medium_b64_h16_n1024_d64": R32, "long_b4_h32_n4096_d128": R32,
+            "gqa_short_b64_hq32_hkv4_n200_d128": R32}
+    if n_cu <= 256:
+        want.update({"gqa_b2_hq32_hkv8_n8192_d128": R64, "long_context_b1_h8_n32768_d128": R64})
+    if n_cu > 128:
+        want["one_head_b1_h1_n32768_d128"] = R32     # 128 workgroups of 256 rows
+    for name, kern in want.items():
+        w = workloads.WORKLOADS[name]
+        assert attn.attn_fwd_plan(w.B, w.Hq, w.Hkv, w.N, w.d) == kern, name
+    # the rule's edges: N, head dim, and the grid against the compute units
+    rows_for = lambda g_rows: -(-g_rows // 256)        # 256-row workgroups of one group
+    hkv = -(-n_cu // rows_for(4 * 8192))                 # just enough groups to fill the CUs
+    assert attn.attn_fwd_plan(1, 4 * hkv, hkv, 8192, 128) == R64
+    assert attn.attn_fwd_plan(1, 4 * hkv, hkv, 8191, 128) == R32
+    assert attn.attn_fwd_plan(1, 4 * hkv, hkv, 8192, 64) == R32
+    if hkv > 1:
+        assert attn.attn_fwd_plan(1, 4 * (hkv - 1), hkv - 1, 8192, 128) == R32
+
+
 @pytest.mark.parametrize("scale", [1 / math.sqrt(128), -0.05])
 def test_rows64_long_ragged(attn, scale):
     """Head dim 128 with N >= 8192 and a grid of at least one workgroup per CU
     runs the rows64 kernel (shorter keys or smaller grids run rows32): a
     ragged last key tile and a GQA group, sampled rows against the oracle."""
     B, Hq, Hkv, N, d = 1, 16, 4, 8197, 128
+    _rows64_plan(attn, B, Hq, Hkv, N, d)
     _say(f"[parity] rows64 long ragged {B},{Hq},{Hkv},{N},{d} scale={scale}")
     q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=8197)
     o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), scale)
     torch.cuda.synchronize()
     check_sampled(q, k, v, o.cpu(), lse.cpu(), scale, "bf16", seed=5)
+
+
+@pytest.mark.parametrize("pattern", ["ramp", "steps", "falling"])
+def test_rows64_moving_max(attn, pattern):
+    """The rows64 kernel's rescale path: key norms that ramp up or double
+    every 1024 keys along a long row (the running max moves by more than the
+    kernel's threshold on later tiles and the accumulators are rescaled), and
+    the reverse, on a shape that runs rows64, every head checked on sampled
+    rows."""
+    B, Hq, Hkv, N, d = 1, 16, 4, 8200, 128
+    _rows64_plan(attn, B, Hq, Hkv, N, d)
+    _say(f"[parity] rows64 moving max {pattern} {B},{Hq},{Hkv},{N},{d}")
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=8200)
+    j = torch.arange(N, dtype=torch.float32)
+    if pattern == "ramp":
+        f = 1.0 + j / 512.0
+    elif pattern == "steps":
+        f = 2.0 ** torch.clamp(j // 1024, max=6)
+    else:
+        f = 2.0 ** -torch.clamp(j // 1024, max=6) * 8.0
+    k = (k.float() * f[None, None, :, None]).to(torch.bfloat16).contiguous()
+    scale = 1 / math.sqrt(d)
+    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    check_sampled(q, k, v, o, lse, scale, "bf16", seed=6)
+    check_every_head(q, k, v, o, lse, scale, "bf16", seed=6, n_rows=8)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -392,6 +467,7 @@ def test_full_workload(attn, name):
     o, lse = o1.cpu(), l1.cpu()
     del o1, o2, l1, l2
     r = check_sampled(q, k, v, o, lse, scale, w.dtype, seed=w.seed)
+    check_every_head(q, k, v, o, lse, scale, w.dtype, seed=w.seed)
     _say(f"[parity] {name}: {r}")
 
 

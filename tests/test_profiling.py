@@ -73,3 +73,43 @@ def test_counter_summary_matches_only_its_own_kernel_sources(tmp_path):
     assert bench.traffic_from_profiles("long_b4_h32_n4096_d128", 0, str(tmp_path)) is None
     # the d = 64 and d = 128 kernels are built from different sources
     assert bench.kernel_source_hash(w) != bench.kernel_source_hash("long_b4_h32_n4096_d128")
+
+
+def test_counters_sum_the_kernels_of_one_call(tmp_path):
+    """The materialising path's three kernels: one call's bytes are the sum of
+    each kernel's median dispatch, every one scaled by the copy calibration."""
+    _counter_csv(tmp_path / "cf.csv", profiling.COPY_KERNEL, [512.0])
+    _counter_csv(tmp_path / "cw.csv", profiling.COPY_KERNEL, [1024.0])
+    rows_f = [("qk_bf16_kernel<128>", 10.0), ("softmax_rows_wave_kernel<bf16>", 20.0),
+              ("pv_bf16_kernel<128, true>", 30.0)] * 2
+    rows_w = [("qk_bf16_kernel<128>", 1.0), ("softmax_rows_wave_kernel<bf16>", 2.0),
+              ("pv_bf16_kernel<128, true>", 3.0)] * 2
+    for name, rows in (("f.csv", rows_f), ("w.csv", rows_w)):
+        with open(tmp_path / name, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Value"])
+            w.writeheader()
+            for k, v in rows:
+                w.writerow({"Kernel_Name": k, "Counter_Value": v})
+    rec = profiling.counters_summary("wl", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                     str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), 1,
+                                     "cmd", "sha", ("qk_bf16", "softmax_rows", "pv_bf16"))
+    assert rec["hbm_read_bytes_per_launch"] == (10 + 20 + 30) * 1024 * 2
+    assert rec["hbm_write_bytes_per_launch"] == (1 + 2 + 3) * 1024
+    assert rec["per_kernel"]["softmax_rows"]["read_bytes"] == 20 * 1024 * 2
+    with pytest.raises(ValueError):
+        profiling.counters_summary("wl", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                   str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), 1,
+                                   "cmd", "sha", ("no_such_kernel",))
+
+
+def test_materialized_counters_match_their_own_sources(tmp_path):
+    import bench
+
+    w = "long_b4_h32_n4096_d128"
+    rec = {"kernel_source_sha": bench.materialized_source_hash(),
+           "hbm_read_bytes_per_launch": 7, "hbm_write_bytes_per_launch": 5}
+    path = tmp_path / f"attn_fwd_materialized_{w}_counters.json"
+    path.write_text(json.dumps(rec))
+    assert bench.materialized_traffic_from_profiles(w, str(tmp_path)) == (7, 5)
+    path.write_text(json.dumps(dict(rec, kernel_source_sha="stale")))
+    assert bench.materialized_traffic_from_profiles(w, str(tmp_path)) is None
