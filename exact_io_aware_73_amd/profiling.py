@@ -5,10 +5,13 @@
     python -m exact_io_aware_73_amd.profiling counters <workload> <fetch.csv> <write.csv>
         <copy_fetch.csv> <copy_write.csv> <copy_mib> <out.json> "<commands>" <kernel_source_sha>
         [<kernel>,<kernel>,...]
+    python -m exact_io_aware_73_amd.profiling sq <out.txt> "<title and commands>" <kernel>
+        <key tiles per wave> <pmc.csv> [<pmc.csv> ...]
 
 ``stats`` turns a ``--kernel-trace --stats`` CSV into a short text table;
 given the per-dispatch trace and K, it adds each kernel's mean over its
 last K dispatches (the timed steps of a bench run, after its warm-up).
+``sq`` summarises SQ / GRBM counter runs of one kernel per wave-tile.
 ``counters`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
 the fused kernel, and the same two counters read on a plain device copy of
 known size, into HBM bytes per launch: each counter (KiB per dispatch) is
@@ -102,6 +105,51 @@ def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_
     return rec
 
 
+def sq_summary(csv_paths, kernel_substr: str, tiles_per_wave: int, n_simd: int = 1024,
+               n_xcd: int = 8) -> dict:
+    """Per-dispatch SQ / GRBM counters of one kernel (summed over the
+    counter instances), the dispatch duration, and figures per wave-tile
+    (one wave's pass over one key tile): instructions by kind, the matrix-
+    core and vector-ALU busy cycles, their overlap, and the clock
+    (GRBM_GUI_ACTIVE per XCD over the dispatch time).  Cycle counters that
+    count in units of four cycles (SQ_ACTIVE_INST_*, SQ_WAIT_*, SQ_WAVE_CYCLES)
+    are scaled by 4."""
+    per = {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            if kernel_substr not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault((path, int(r["Dispatch_Id"])), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            d["_name"] = r["Kernel_Name"]
+    if not per:
+        raise ValueError(f"no dispatch of {kernel_substr!r}")
+    merged = {}
+    for (path, _), d in per.items():
+        for k, v in d.items():
+            merged.setdefault(k, []).append(v)
+    med = {k: statistics.median(v) for k, v in merged.items() if k != "_name"}
+    waves = med.get("SQ_WAVES")
+    out = {"kernel": merged["_name"][0], "dispatches": len(merged["_ns"]), "median": med}
+    if waves:
+        wt = waves * tiles_per_wave
+        q4 = {"SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY",
+              "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"}
+        out["per_wave_tile"] = {k: round(v * (4 if k in q4 else 1) / wt, 1) for k, v in med.items()
+                                if k.startswith("SQ_") and k != "SQ_WAVES"}
+    if "GRBM_GUI_ACTIVE" in med:
+        cyc = med["GRBM_GUI_ACTIVE"] / n_xcd
+        out["clock_ghz"] = round(cyc / med["_ns"], 3)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            out["mfma_busy"] = round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * n_simd), 3)
+        if "SQ_ACTIVE_INST_VALU" in med:
+            out["valu_busy"] = round(4 * med["SQ_ACTIVE_INST_VALU"] / (cyc * n_simd), 3)
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in med:
+            out["mfma_valu_coexec"] = round(med["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cyc * n_simd), 3)
+    return out
+
+
 def main(argv):
     if argv[0] == "stats":
         src, out, cmd = argv[1:4]
@@ -116,6 +164,12 @@ def main(argv):
         json.dump(rec, open(out, "w"), indent=1)
         print(json.dumps({k: rec[k] for k in ("workload", "hbm_read_bytes_per_launch",
                                                "hbm_write_bytes_per_launch")}))
+    elif argv[0] == "sq":
+        out, title, kern, tiles = argv[1:5]
+        rec = sq_summary(argv[5:], kern, int(tiles))
+        with open(out, "w") as f:
+            f.write(title.rstrip() + "\n\n" + json.dumps(rec, indent=1) + "\n")
+        print(json.dumps({k: rec[k] for k in rec if k not in ("median", "per_wave_tile")}))
     else:
         raise SystemExit(__doc__)
 
