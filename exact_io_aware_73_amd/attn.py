@@ -14,6 +14,8 @@ Entry points carry the C names and take tensors instead of raw pointers:
     attn_fwd_split_workspace_bytes(B, Hq, N, d, n_split)
     attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, stream=None)   bf16
     attn_bwd_workspace_bytes(B, Hq, N)
+    attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale, stream=None)   bf16, no workspace
+    attn_bwd_noalloc_max_rows()
     attn_fwd_fp8(q8, k8, vt8, o, lse, q_scale, k_scale, v_scale, scale, stream=None)
     attn_device_info(device=None) -> (compute units, XCDs)
     attn_fwd_plan(B, Hq, Hkv, N, d, device=None) -> ATTN_KERNEL_ROWS32 / _ROWS64
@@ -63,6 +65,10 @@ _lib.attn_fwd_fp8.restype = _I
 _lib.attn_strerror.argtypes = [_I]
 _lib.attn_strerror.restype = ctypes.c_char_p
 
+_lib.attn_bwd_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]
+_lib.attn_bwd_noalloc.restype = _I
+_lib.attn_bwd_noalloc_max_rows.argtypes = []
+_lib.attn_bwd_noalloc_max_rows.restype = _U64
 _lib.attn_device_info.argtypes = [ctypes.POINTER(_I), ctypes.POINTER(_I)]
 _lib.attn_device_info.restype = _I
 _lib.attn_fwd_plan.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_I)]
@@ -70,7 +76,7 @@ _lib.attn_fwd_plan.restype = _I
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_GQA, ATTN_ERR_HEADDIM = 0, 1, 2, 3, 4
 ATTN_ERR_SCALE, ATTN_ERR_ALIGN, ATTN_ERR_HIP, ATTN_ERR_ALIAS = 5, 6, 7, 8
-ATTN_ERR_SPLIT, ATTN_ERR_WORKSPACE = 9, 10
+ATTN_ERR_SPLIT, ATTN_ERR_WORKSPACE, ATTN_ERR_SCRATCH = 9, 10, 11
 ATTN_MAX_SPLIT = 64
 ATTN_KERNEL_ROWS32, ATTN_KERNEL_ROWS64 = 1, 2
 
@@ -273,6 +279,35 @@ def attn_fwd_plan(B, Hq, Hkv, N, d, device=None) -> int:
         st = _lib.attn_fwd_plan(int(B), int(Hq), int(Hkv), int(N), int(d), ctypes.byref(kern))
     _raise(st, "attn_fwd_plan")
     return kern.value
+
+
+def attn_bwd_noalloc_max_rows() -> int:
+    """Largest B * Hq * N that attn_bwd_noalloc accepts."""
+    return int(_lib.attn_bwd_noalloc_max_rows())
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale, stream=None):
+    """Gradients of attn_fwd with no workspace argument: the library's fixed
+    scratch buffer holds the row sums (C: attn_bwd_noalloc).  Calls that may
+    overlap on one device race on that buffer."""
+    fn_name = "attn_bwd_noalloc"
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    for name, t, dt, shape in (("q", q, torch.bfloat16, q.shape), ("o", o, torch.bfloat16, q.shape),
+                               ("dout", dout, torch.bfloat16, q.shape),
+                               ("dq", dq, torch.bfloat16, q.shape), ("dk", dk, torch.bfloat16, k.shape),
+                               ("dv", dv, torch.bfloat16, k.shape), ("k", k, torch.bfloat16, k.shape),
+                               ("v", v, torch.bfloat16, k.shape), ("lse", lse, torch.float32, (B, Hq, N))):
+        if t.dtype != dt:
+            raise ValueError(f"{fn_name}: {name} must be {dt}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{fn_name}: {name} must be {tuple(shape)}, got {tuple(t.shape)}")
+        if t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{fn_name}: {name} must be contiguous on {q.device}")
+    with torch.cuda.device(q.device):
+        st = _lib.attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d,
+                                   ctypes.c_float(float(scale)), _stream_handle(stream, q.device))
+    _raise(st, fn_name)
 
 
 def _scale(scale, d):

@@ -54,6 +54,43 @@ hipError_t device_facts(DeviceFacts* out) {
   return out->err;
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The fixed scratch buffer of attn_bwd_noalloc: device memory the library
+// owns, one copy per device (held until the process ends), so that entry
+// point allocates nothing.  It holds the backward's per-row dot products
+// D = rowsum(dO * O), 4 bytes per query row; every row is written before it
+// is read, so nothing needs clearing between calls.
+namespace attn {
+constexpr uint64_t kScratchBytes = 16ull << 20;
+__device__ __align__(256) float scratch[kScratchBytes / 4];
+}  // namespace attn
+
+namespace {
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's scratch copy: looked up once per device,
+// with that device current.  The host-side name of the array is a stand-in,
+// not a device address, so only this pointer is ever passed to kernels.
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(attn::scratch));
+    g_scratch[dev] = (g_scratch_err[dev] == hipSuccess) ? p : nullptr;
+    if (g_scratch_err[dev] == hipSuccess && p == nullptr) g_scratch_err[dev] = hipErrorInvalidSymbol;
+  });
+  *out = g_scratch[dev];
+  return g_scratch_err[dev];
+}
+
 struct Range {
   uintptr_t lo, hi;   // [lo, hi)
 };
@@ -221,9 +258,11 @@ int split_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   return to_status(attn::launch_split_merge_bf16(a));
 }
 
+// ws == nullptr with noalloc: the row dot products go to the library's
+// fixed scratch buffer instead of a caller workspace.
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, void* ws, uint64_t ws_bytes, int B,
-             int Hq, int Hkv, int N, int d, float scale, void* stream) {
+             int Hq, int Hkv, int N, int d, float scale, void* stream, bool noalloc = false) {
   // the forward-shaped arguments first (q, k, v, o, lse as attn_fwd checks them)
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
   if (st != ATTN_OK) return st;
@@ -234,7 +273,11 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   if (attn::bwd_grid(B, Hq, Hkv, N) > kMaxWorkgroups || rows * 8 / 256 + 1 > kMaxWorkgroups)
     return ATTN_ERR_SHAPE;
   const uint64_t need = rows * 4;
-  if (!ws || !aligned(ws, 16) || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (noalloc) {
+    if (need > attn::kScratchBytes) return ATTN_ERR_SCRATCH;
+  } else if (!ws || !aligned(ws, 16) || ws_bytes < need) {
+    return ATTN_ERR_WORKSPACE;
+  }
   auto rng = [](const void* ptr, uint64_t bytes) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
     return Range{lo, lo + (uintptr_t)bytes};
@@ -242,7 +285,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   const uint64_t qo = rows * d * 2, kv = (uint64_t)B * Hkv * N * d * 2;
   const Range in[6] = {rng(q, qo), rng(k, kv), rng(v, kv), rng(o, qo), rng(lse, rows * 4),
                        rng(dout, qo)};
-  const int n_out = 4;
+  const int n_out = noalloc ? 3 : 4;   // the scratch buffer is the library's own
   const Range out[4] = {rng(dq, qo), rng(dk, kv), rng(dv, kv), rng(ws, need)};
   for (int i = 0; i < n_out; ++i) {
     for (const Range& r : in)
@@ -252,6 +295,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   }
   DeviceFacts f;
   if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
+  if (noalloc && scratch_ptr(&ws) != hipSuccess) return ATTN_ERR_HIP;
   attn::FwdArgs a = make_args(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), nullptr,
                               nullptr, B, Hq, Hkv, N, d, scale, f.n_xcd, stream);
   attn::BwdArgs g;
@@ -379,6 +423,21 @@ ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o
   }
 }
 
+ATTN_API int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int N, int d, float scale, void* stream) {
+  try {
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, nullptr, 0, B, Hq, Hkv, N, d, scale,
+                    stream, true);
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+ATTN_API unsigned long long attn_bwd_noalloc_max_rows(void) {
+  return attn::kScratchBytes / 4;
+}
+
 ATTN_API unsigned long long attn_bwd_workspace_bytes(int B, int Hq, int N) {
   if (B < 1 || Hq < 1 || N < 1) return 0;
   return (uint64_t)B * Hq * (uint64_t)N * 4u;
@@ -424,6 +483,8 @@ ATTN_API const char* attn_strerror(int status) {
     case ATTN_ERR_HIP: return "the HIP runtime reported an error (launch or device query)";
     case ATTN_ERR_SPLIT: return "n_split must be in [1, ATTN_MAX_SPLIT]";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned or too small";
+    case ATTN_ERR_SCRATCH:
+      return "the problem needs more than the library's fixed scratch buffer (B*Hq*N rows)";
     default: return "unknown status";
   }
 }

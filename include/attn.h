@@ -73,7 +73,8 @@ typedef enum {
   ATTN_ERR_HIP = 7,      /* the HIP runtime reported an error (a launch, or a device query) */
   ATTN_ERR_ALIAS = 8,    /* an output overlaps an input or another output */
   ATTN_ERR_SPLIT = 9,    /* n_split outside [1, ATTN_MAX_SPLIT] */
-  ATTN_ERR_WORKSPACE = 10 /* workspace NULL, misaligned or smaller than required */
+  ATTN_ERR_WORKSPACE = 10, /* workspace NULL, misaligned or smaller than required */
+  ATTN_ERR_SCRATCH = 11  /* more rows than the fixed scratch buffer of attn_bwd_noalloc holds */
 } attn_status_t;
 
 /* Largest number of key ranges the split-KV entry point accepts. */
@@ -223,6 +224,28 @@ ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o
 
 /* attn_bwd_workspace_bytes -- B * Hq * N * 4; 0 for B, Hq or N < 1. */
 ATTN_API unsigned long long attn_bwd_workspace_bytes(int B, int Hq, int N);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving or training loops, harnesses that forbid allocation).  The same
+ * kernels and results as attn_bwd; the per-row dot products go to a fixed
+ * scratch buffer inside the library (16 MiB of device memory per device,
+ * held until the process ends), so this call allocates nothing.
+ *
+ * Limit: B * Hq * N <= attn_bwd_noalloc_max_rows() (4194304 rows), else
+ * ATTN_ERR_SCRATCH before any HIP call.  Every call on one device shares that
+ * device's buffer: two calls that may run at the same time on one device
+ * (different streams, or different threads without ordering) race and give
+ * wrong gradients; order them on one stream.  Arguments, layouts and the
+ * other errors as attn_bwd.
+ */
+ATTN_API int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int N, int d, float scale, void* stream);
+
+/* attn_bwd_noalloc_max_rows -- the largest B * Hq * N attn_bwd_noalloc accepts. */
+ATTN_API unsigned long long attn_bwd_noalloc_max_rows(void);
 
 /*
  * attn_device_info -- the device facts the launches use, for the calling

@@ -50,18 +50,21 @@ def test_header_declares_the_entry_points():
     assert set(_declared()) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_materialized",
                                 "attn_fwd_materialized_f32", "attn_fwd_split",
                                 "attn_fwd_split_workspace_bytes", "attn_bwd",
-                                "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_device_info",
+                                "attn_bwd_workspace_bytes", "attn_bwd_noalloc",
+                                "attn_bwd_noalloc_max_rows", "attn_fwd_fp8", "attn_device_info",
                                 "attn_fwd_plan", "attn_strerror"}
 
 
 def test_status_numbering_is_pinned():
     """The status values are part of the ABI: 0 - 7 as the boundary was
     specified (ATTN_ERR_HIP = 7), the three codes added with the alias check,
-    the split-KV and the workspace arguments after them.  The binding's
+    the split-KV and the workspace arguments after them, then the fixed
+    scratch buffer's limit.  The binding's
     constants carry the same values."""
     want = {"ATTN_OK": 0, "ATTN_ERR_NULL": 1, "ATTN_ERR_SHAPE": 2, "ATTN_ERR_GQA": 3,
             "ATTN_ERR_HEADDIM": 4, "ATTN_ERR_SCALE": 5, "ATTN_ERR_ALIGN": 6, "ATTN_ERR_HIP": 7,
-            "ATTN_ERR_ALIAS": 8, "ATTN_ERR_SPLIT": 9, "ATTN_ERR_WORKSPACE": 10}
+            "ATTN_ERR_ALIAS": 8, "ATTN_ERR_SPLIT": 9, "ATTN_ERR_WORKSPACE": 10,
+            "ATTN_ERR_SCRATCH": 11}
     assert _status_codes() == want
     src = open(os.path.join(ROOT, "exact_io_aware_73_amd", "attn.py")).read()
     m = re.findall(r"^(ATTN_[\w, ]+?)\s*=\s*([\d, ]+)$", src, re.M)
@@ -207,6 +210,31 @@ def _bwd(lib, q=Q, k=K, v=V, o=O, lse=L, do=DO_, dq=DQ_, dk=DK_, dv=DV_, ws=WB, 
          B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125):
     return lib.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, N, d,
                         ctypes.c_float(scale), None)
+
+
+def _bwd_noalloc(lib, q=Q, k=K, v=V, o=O, lse=L, do=DO_, dq=DQ_, dk=DK_, dv=DV_, B=1, Hq=2, Hkv=1,
+                N=16, d=64, scale=0.125):
+    return lib.attn_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d,
+                                ctypes.c_float(scale), None)
+
+
+def test_bwd_noalloc_limit(lib):
+    lib.attn_bwd_noalloc_max_rows.restype = ctypes.c_ulonglong
+    assert lib.attn_bwd_noalloc_max_rows() == (16 << 20) // 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=(16 << 20) // 4 + 1, Hq=1), "ATTN_ERR_SCRATCH"),
+    (dict(B=2, Hq=8, Hkv=8, N=(16 << 20) // 64 + 1), "ATTN_ERR_SCRATCH"),
+    (dict(do=None), "ATTN_ERR_NULL"), (dict(dq=None), "ATTN_ERR_NULL"), (dict(lse=None), "ATTN_ERR_NULL"),
+    (dict(dk=DK_ + 2), "ATTN_ERR_ALIGN"), (dict(dq=Q), "ATTN_ERR_ALIAS"), (dict(dv=DK_ + 64), "ATTN_ERR_ALIAS"),
+    (dict(Hq=3, Hkv=2), "ATTN_ERR_GQA"), (dict(d=32), "ATTN_ERR_HEADDIM"), (dict(N=0), "ATTN_ERR_SHAPE"),
+    (dict(scale=math.nan), "ATTN_ERR_SCALE"),
+])
+def test_bwd_noalloc_rejects(lib, kw, code):
+    lib.attn_bwd_noalloc.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float,
+                                                                                   ctypes.c_void_p]
+    assert _bwd_noalloc(lib, **kw) == _status_codes()[code]
 
 
 def test_bwd_workspace_bytes(lib):
