@@ -302,7 +302,7 @@ def main():
     with torch.cuda.stream(stream):
         n_warm, warm_ms = warm_up(step, args.warmup, args.min_warmup_ms)
         ms_step, ev_mean, ev_min, ev_med = time_launches(step, stream, args.steps, 0)
-    n_cu, n_xcd = attn.attn_device_info()
+    n_cu, n_xcd, l2_bytes = attn.attn_device_info()
     kernel = ("attn_fwd_f32_kernel" if w.dtype != "bf16" else
               "attn_fwd_fp8_kernel" if fp8 else
               "attn_fwd_bf16_rows64_split_kernel + attn_split_merge_kernel" if args.split else
@@ -328,7 +328,7 @@ def main():
                 "hbm_gbps": (round(traffic / (ev_mean * 1e-3) / 1e9, 1) if traffic else None),
                 "hbm_frac": (round(traffic / (ev_mean * 1e-3) / 1e9 / acc.PEAK_HBM_GBPS, 4)
                              if traffic else None),
-                "device": {"compute_units": n_cu, "xcds": n_xcd}}
+                "device": {"compute_units": n_cu, "xcds": n_xcd, "l2_bytes": l2_bytes}}
 
     materialized = None
     sp_bytes = w.B * w.Hq * w.N * w.N * (4 + w.elem_bytes)

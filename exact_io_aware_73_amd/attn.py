@@ -17,7 +17,7 @@ Entry points carry the C names and take tensors instead of raw pointers:
     attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale, stream=None)   bf16, no workspace
     attn_bwd_noalloc_max_rows()
     attn_fwd_fp8(q8, k8, vt8, o, lse, q_scale, k_scale, v_scale, scale, stream=None)
-    attn_device_info(device=None) -> (compute units, XCDs)
+    attn_device_info(device=None) -> (compute units, XCDs, L2 bytes)
     attn_fwd_plan(B, Hq, Hkv, N, d, device=None) -> ATTN_KERNEL_ROWS32 / _ROWS64
     attn_strerror(status)
 
@@ -69,7 +69,7 @@ _lib.attn_bwd_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I
 _lib.attn_bwd_noalloc.restype = _I
 _lib.attn_bwd_noalloc_max_rows.argtypes = []
 _lib.attn_bwd_noalloc_max_rows.restype = _U64
-_lib.attn_device_info.argtypes = [ctypes.POINTER(_I), ctypes.POINTER(_I)]
+_lib.attn_device_info.argtypes = [ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_I)]
 _lib.attn_device_info.restype = _I
 _lib.attn_fwd_plan.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_I)]
 _lib.attn_fwd_plan.restype = _I
@@ -263,12 +263,13 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, stream=None):
 
 
 def attn_device_info(device=None):
-    """(compute units, XCDs) of a device as the library reads them (C: attn_device_info)."""
-    cu, xcd = _I(0), _I(0)
+    """(compute units, XCDs, L2 bytes of one XCD) of a device as the library
+    reads them (C: attn_device_info)."""
+    cu, xcd, l2 = _I(0), _I(0), _I(0)
     with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
-        st = _lib.attn_device_info(ctypes.byref(cu), ctypes.byref(xcd))
+        st = _lib.attn_device_info(ctypes.byref(cu), ctypes.byref(xcd), ctypes.byref(l2))
     _raise(st, "attn_device_info")
-    return cu.value, xcd.value
+    return cu.value, xcd.value, l2.value
 
 
 def attn_fwd_plan(B, Hq, Hkv, N, d, device=None) -> int:

@@ -27,6 +27,7 @@ constexpr uint64_t kMaxWorkgroups = (1ull << 32) / 256 - 1;
 struct DeviceFacts {
   int n_cu = 0;
   int n_xcd = 1;
+  int l2_bytes = 0;   // the L2 cache of one XCD (the launch order keeps K/V there)
   hipError_t err = hipSuccess;
 };
 constexpr int kMaxDevices = 64;
@@ -41,13 +42,15 @@ hipError_t device_facts(DeviceFacts* out) {
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::call_once(g_facts_once[dev], [dev] {
     DeviceFacts f;
-    int cu = 0, xcc = 0;
+    int cu = 0, xcc = 0, l2 = 0;
     f.err = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (f.err == hipSuccess)
       f.err = hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev);
+    if (f.err == hipSuccess) f.err = hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, dev);
     if (f.err == hipSuccess && cu < 1) f.err = hipErrorInvalidDevice;
     f.n_cu = cu;
     f.n_xcd = xcc > 0 ? xcc : 1;
+    f.l2_bytes = l2 > 0 ? l2 : 0;
     g_facts[dev] = f;
   });
   *out = g_facts[dev];
@@ -184,8 +187,10 @@ int fwd_impl(bool bf16, const void* q, const void* k, const void* v, void* o, fl
   if (st != ATTN_OK) return st;
   DeviceFacts f;
   if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
-  const attn::FwdArgs a =
+  attn::FwdArgs a =
       make_args(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, d, scale, f.n_xcd, stream);
+  a.n_cu = f.n_cu;
+  a.l2_bytes = f.l2_bytes;
   if (!bf16) return to_status(attn::launch_fwd_f32(a));
   return to_status(attn::fwd_bf16_use_rows64(B, Hq, Hkv, N, d, f.n_cu)
                        ? attn::launch_fwd_bf16_rows64(a)
@@ -443,12 +448,13 @@ ATTN_API unsigned long long attn_bwd_workspace_bytes(int B, int Hq, int N) {
   return (uint64_t)B * Hq * (uint64_t)N * 4u;
 }
 
-ATTN_API int attn_device_info(int* n_cu, int* n_xcd) {
+ATTN_API int attn_device_info(int* n_cu, int* n_xcd, int* l2_bytes) {
   try {
     DeviceFacts f;
     if (device_facts(&f) != hipSuccess) return ATTN_ERR_HIP;
     if (n_cu) *n_cu = f.n_cu;
     if (n_xcd) *n_xcd = f.n_xcd;
+    if (l2_bytes) *l2_bytes = f.l2_bytes;
     return ATTN_OK;
   } catch (...) {
     return ATTN_ERR_HIP;

@@ -18,6 +18,8 @@ struct FwdArgs {
   int B, Hq, Hkv, N, d;
   float scale;
   int n_xcd;
+  int n_cu = 0;        // compute units of the device
+  int l2_bytes = 0;    // L2 cache of one XCD, bytes
   // split-KV path only: the key ranges, their length (whole tiles) and the
   // fp32 partial results [n_split][B*Hq*N][d] and [n_split][B*Hq*N]
   int n_split = 1;

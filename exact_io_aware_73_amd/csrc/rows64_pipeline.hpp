@@ -48,7 +48,14 @@
 //    kRescaleLog2 (softmax is unchanged by any common shift of a row, the
 //    basis of the rescale rule), so the rescale of the accumulator is rare.
 //  * Workgroups of one K/V head are numbered consecutively and remapped so
-//    they run on one XCD and share its L2.
+//    they run on one XCD and share its L2.  One XCD holds 32 x 256 query rows
+//    at a time, so a head with more query rows streams its K/V through that
+//    L2 once per round of workgroups.  Where a head's K/V fits the L2, every
+//    other round streams the keys in reverse order, so it starts on the tiles
+//    the round before left in the L2 (the result is the same up to the
+//    rounding order), and O is stored as whole rows through LDS with a
+//    non-temporal hint; Q is always loaded with one.  Neither then displaces
+//    K/V from the L2, and no O line is written back in pieces.
 #pragma once
 
 #ifndef ATTN_ROWS64_SPLIT
@@ -85,6 +92,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
@@ -154,6 +162,7 @@ struct WaveState {
   int voff[G::kDB];                // LDS byte offsets of the V^T transposing reads (rows +0..3)
   int voff8[D == 128 ? 1 : G::kDB];  // the same for rows +8..11 (d = 64 only, see hi_off)
   int dvoff[G::kDma];              // byte offsets of this lane's direct loads within a tile
+  int rev_last;                    // > 0: keys run in reverse order; the first key of the last tile
 };
 
 // Byte offset of the transposing V read of rows +8..11 for d block db.  For
@@ -172,8 +181,19 @@ __device__ __forceinline__ int hi_off(const WaveState<D>& w, int db) {
 // in flight and does not stall the LDS reads of the other slots behind it;
 // the step's own vmcnt wait and barrier order these loads against readers.
 template <int D>
-__device__ __forceinline__ void dma_tile(const int* dvoff, const __bf16* head, int j0, int N,
+__device__ __forceinline__ void dma_tile_at(const int* dvoff, const __bf16* head, int j0, int N,
+                                            uint32_t lds_byte, int wave);
+// Tile j0 / kBc of the key order this wave runs: in reverse order the tiles
+// are taken from the end, and tiles past the last still read nothing.
+template <int D>
+__device__ __forceinline__ void dma_tile(const WaveState<D>& w, const __bf16* head, int j0, int N,
                                          uint32_t lds_byte, int wave) {
+  if (w.rev_last > 0) j0 = j0 > w.rev_last ? N : w.rev_last - j0;
+  dma_tile_at<D>(w.dvoff, head, j0, N, lds_byte, wave);
+}
+template <int D>
+__device__ __forceinline__ void dma_tile_at(const int* dvoff, const __bf16* head, int j0, int N,
+                                            uint32_t lds_byte, int wave) {
   using G = FGeo<D>;
   // every operand of the buffer resource is wave-uniform (SGPRs)
   const int rows = __builtin_amdgcn_readfirstlane(max(0, min(N - j0, kBc)));
@@ -353,9 +373,9 @@ __device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, const __bf16
   if (kSlotsUsed > 0) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      if (u == kDmaK) dma_tile<D>(w.dvoff, kh, (j + kSlots) * kBc, N, lds + kJ4 * kTileB, wave);
+      if (u == kDmaK) dma_tile<D>(w, kh, (j + kSlots) * kBc, N, lds + kJ4 * kTileB, wave);
       if (u == kDmaV)
-        dma_tile<D>(w.dvoff, vh, (j + kSlots - 2) * kBc, N,
+        dma_tile<D>(w, vh, (j + kSlots - 2) * kBc, N,
                     lds + (kSlots + (kJ4 + kSlots - 2) % kSlots) * kTileB, wave);
       if (u + kAhead < kU) {
         if (kQK) kf[u + kAhead] = lds_k(k_rd, w.koff[u + kAhead]);
@@ -383,8 +403,8 @@ __device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, const __bf16
       }
     }
   } else {
-    dma_tile<D>(w.dvoff, kh, (j + kSlots) * kBc, N, lds + kJ4 * kTileB, wave);
-    dma_tile<D>(w.dvoff, vh, (j + kSlots - 2) * kBc, N,
+    dma_tile<D>(w, kh, (j + kSlots) * kBc, N, lds + kJ4 * kTileB, wave);
+    dma_tile<D>(w, vh, (j + kSlots - 2) * kBc, N,
                 lds + (kSlots + (kJ4 + kSlots - 2) % kSlots) * kTileB, wave);
 #pragma unroll
     for (int t = 0; t < kTasks; ++t) softmax_task<D, kNeg, kMask, kPar>(t, w, sc, c_log2, valid, hh);
@@ -482,12 +502,14 @@ void attn_fwd_bf16_rows64_split_kernel(const __bf16* __restrict__ q,
                                        int chunk_keys, int64_t n_rows, float* __restrict__ part_o,
                                        float* __restrict__ part_lse) {
 #else
+// rev_every: 0, or the workgroups one XCD runs at a time (one round); odd
+// rounds then stream the keys in reverse order (N a multiple of kBc only).
 template <int D, bool kNeg>
 __global__ __launch_bounds__(kFThreads, 1)
 void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                           const __bf16* __restrict__ v, __bf16* __restrict__ o,
                           float* __restrict__ lse, int Hq, int Hkv, int N, float c_log2,
-                          int n_qtiles, uint32_t n_xcd) {
+                          int n_qtiles, uint32_t n_xcd, uint32_t rev_every) {
 #endif
   using G = FGeo<D>;
   // K slots then V slots, kBc x D bf16 each
@@ -535,6 +557,14 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
   const int n_tiles = (ATTN_KEYS + kBc - 1) / kBc;
 
   WaveState<D> w;
+#if ATTN_ROWS64_SPLIT
+  w.rev_last = 0;
+#else
+  // this workgroup's round on its XCD (workgroups are dealt round-robin)
+  const bool stream_hints = rev_every != 0;
+  w.rev_last = (stream_hints && (((blockIdx.x / n_xcd) / rev_every) & 1u) != 0)
+                   ? (n_tiles - 1) * kBc : 0;
+#endif
   // ---- Q^T fragments: lane holds d = 16 s + 8 hh .. +7 of its queries -----
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
@@ -543,7 +573,9 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
     const __bf16* qp = q + (head_q + (qvalid ? qrow : 0)) * D + 8 * hh;
 #pragma unroll
     for (int st = 0; st < G::kKSteps; ++st) {
-      u32x4 u = qvalid ? *reinterpret_cast<const u32x4*>(qp + 16 * st) : u32x4{0u, 0u, 0u, 0u};
+      // read once: a streaming load, so Q does not displace K/V lines from the L2
+      u32x4 u = qvalid ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qp + 16 * st))
+                       : u32x4{0u, 0u, 0u, 0u};
       w.qf[qb][st] = as_bf16x8(u);
     }
   }
@@ -586,10 +618,10 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
   // ---- prologue: K tiles 0 .. S-1 and V tiles 0 .. S-3 in flight; S of tile 0
   constexpr uint32_t kTileB = G::kTile * 2;
 #pragma unroll
-  for (int t = 0; t < kSlots; ++t) dma_tile<D>(w.dvoff, kh, t * kBc, ATTN_KEYS, lds + t * kTileB, wave);
+  for (int t = 0; t < kSlots; ++t) dma_tile<D>(w, kh, t * kBc, ATTN_KEYS, lds + t * kTileB, wave);
 #pragma unroll
   for (int t = 0; t < kSlots - 2; ++t)
-    dma_tile<D>(w.dvoff, vh, t * kBc, ATTN_KEYS, lds + (kSlots + t) * kTileB, wave);
+    dma_tile<D>(w, vh, t * kBc, ATTN_KEYS, lds + (kSlots + t) * kTileB, wave);
   // K tiles 0 and 1 must have landed: S of tile 0 reads K slot 0 here and
   // step 0 reads K slot 1 (for S of tile 1) before its own wait; the other
   // 2 kSlots - 4 tiles may still be in flight
@@ -623,6 +655,10 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
   }
   // loads past the last tile may still be writing LDS: drain before exit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#if !ATTN_ROWS64_SPLIT
+  // the epilogue may stage O in the ring: every wave must be done reading it
+  if (stream_hints) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
 
   // ---- epilogue: O = O~ / l, lse = (m + log2 l) ln 2 ------------------------
 #pragma unroll
@@ -647,8 +683,38 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
       if (hh == 0) part_lse[prow] = (w.m[qb] + log2_fast(l_tot)) * 0.69314718055994531f;
     }
 #else
-    if (qrow < n_qrows) {
-      const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / l_tot;
+    if (stream_hints) {
+      // O through LDS: the wave stages its block's 32 rows (rows of D bf16 +
+      // 16 bytes, against bank conflicts), then every store writes whole
+      // rows, non-temporal (partial-line stores left in the L2 would be
+      // written back piecemeal)
+      constexpr int kRowB = D * 2 + 16;
+      const uint32_t stage = lds + (uint32_t)(wave * 32 * kRowB);
+#pragma unroll
+      for (int db = 0; db < G::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u32x2 wv;
+          wv[0] = pack_bf16x2(w.oacc[qb][db][4 * r + 0] * inv, w.oacc[qb][db][4 * r + 1] * inv);
+          wv[1] = pack_bf16x2(w.oacc[qb][db][4 * r + 2] * inv, w.oacc[qb][db][4 * r + 3] * inv);
+          *(lds_u32x2*)(uintptr_t)(stage + l32 * kRowB + (db * 32 + 8 * r + 4 * hh) * 2) = wv;
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's rows are staged
+      constexpr int kChunks = D / 8;                        // 16-byte chunks per row
+      constexpr int kRowsPer = kWave / kChunks;             // rows per store
+#pragma unroll
+      for (int i = 0; i < 32 / kRowsPer; ++i) {
+        const int rr = i * kRowsPer + lane / kChunks;
+        const int ch = lane % kChunks;
+        const u32x4 v4 = *(const lds_u32x4*)(uintptr_t)(stage + rr * kRowB + ch * 16);
+        const int row = qt * kFBr + wave * kFRows + qb * 32 + rr;
+        if (row < n_qrows)
+          __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(o + (head_q + row) * D + ch * 8));
+      }
+      // the next block's staging writes must not pass these reads
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else if (qrow < n_qrows) {
       __bf16* orow = o + (head_q + qrow) * D;
 #pragma unroll
       for (int db = 0; db < G::kDB; ++db)
@@ -659,8 +725,9 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
           wv[1] = pack_bf16x2(w.oacc[qb][db][4 * r + 2] * inv, w.oacc[qb][db][4 * r + 3] * inv);
           *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * r + 4 * hh) = wv;
         }
-      if (hh == 0) lse[head_q + qrow] = (w.m[qb] + log2_fast(l_tot)) * 0.69314718055994531f;
     }
+    if (qrow < n_qrows && hh == 0)
+      lse[head_q + qrow] = (w.m[qb] + log2_fast(l_tot)) * 0.69314718055994531f;
 #endif
   }
 }

@@ -250,13 +250,16 @@ ATTN_API unsigned long long attn_bwd_noalloc_max_rows(void);
 /*
  * attn_device_info -- the device facts the launches use, for the calling
  * thread's current device: the number of compute units (the fused bf16
- * forward picks its kernel by it) and of XCDs, the dies with their own L2
- * cache over which workgroups are dealt round-robin (the launch order maps
- * the workgroups of one K/V head onto one XCD by it).  Read from the HIP
- * runtime once per device and cached.  n_cu / n_xcd: host pointers, either
- * may be NULL.  ATTN_ERR_HIP when the runtime cannot report them.
+ * forward picks its kernel by it), of XCDs, the dies with their own L2 cache
+ * over which workgroups are dealt round-robin (the launch order maps the
+ * workgroups of one K/V head onto one XCD by it), and the L2 bytes the HIP
+ * runtime reports (one XCD's; the head dim 128 kernel streams the keys of
+ * alternate rounds of workgroups in reverse where a K/V head fits it).  Read
+ * from the HIP runtime once per device and cached.  n_cu, n_xcd, l2_bytes:
+ * host pointers, any may be NULL.  ATTN_ERR_HIP when the runtime cannot
+ * report them.
  */
-ATTN_API int attn_device_info(int* n_cu, int* n_xcd);
+ATTN_API int attn_device_info(int* n_cu, int* n_xcd, int* l2_bytes);
 
 /* Fused bf16 forward kernels (the value attn_fwd_plan writes). */
 #define ATTN_KERNEL_ROWS32 1  /* 128 query rows per workgroup, one 32-row block per wave */

@@ -384,8 +384,8 @@ def _rows64_plan(attn, B, Hq, Hkv, N, d):
 def test_kernel_plan_by_shape(attn):
     """Which kernel each bf16 shape runs, asked of the library: rows64 where
     N >= 8192 and the 256-row grid has a workgroup per compute unit."""
-    n_cu, n_xcd = attn.attn_device_info()
-    _say(f"[parity] device: {n_cu} compute units, {n_xcd} XCDs")
+    n_cu, n_xcd, l2 = attn.attn_device_info()
+    _say(f"[parity] device: {n_cu} compute units, {n_xcd} XCDs, L2 {l2} bytes")
     assert n_cu >= 1 and n_xcd >= 1
     R32, R64 = attn.ATTN_KERNEL_ROWS32, attn.ATTN_KERNEL_ROWS64
     want = {"gpt2_medium_b64_h16_n1024_d64": R32, "long_b4_h32_n4096_d128": R32,
@@ -407,6 +407,26 @@ def test_kernel_plan_by_shape(attn):
         assert attn.attn_fwd_plan(1, 4 * (hkv - 1), hkv - 1, 8192, 128) == R32
 
 
+@pytest.mark.parametrize("scale", [1 / math.sqrt(128), -0.05, 0.0])
+def test_rows64_reversed_rounds(attn, scale):
+    """N = 8192, head dim 128, a GQA group per K/V head: the keys fit one XCD's
+    L2, so every other round of workgroups streams them in reverse order and
+    stores O as whole rows through LDS.  1024 workgroups (four rounds), every
+    head checked on sampled rows; bitwise deterministic."""
+    B, Hq, Hkv, N, d = 1, 32, 8, 8192, 128
+    _rows64_plan(attn, B, Hq, Hkv, N, d)
+    _say(f"[parity] rows64 reversed rounds {B},{Hq},{Hkv},{N},{d} scale={scale}")
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=8192 + int(100 * scale))
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, lse = attn.fwd(qd, kd, vd, scale)
+    o2, l2 = attn.fwd(qd, kd, vd, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2), "not deterministic"
+    o, lse = o.cpu(), lse.cpu()
+    check_sampled(q, k, v, o, lse, scale, "bf16", seed=9)
+    check_every_head(q, k, v, o, lse, scale, "bf16", seed=9, n_rows=16)
+
+
 @pytest.mark.parametrize("scale", [1 / math.sqrt(128), -0.05])
 def test_rows64_long_ragged(attn, scale):
     """Head dim 128 with N >= 8192 and a grid of at least one workgroup per CU
@@ -421,17 +441,20 @@ def test_rows64_long_ragged(attn, scale):
     check_sampled(q, k, v, o.cpu(), lse.cpu(), scale, "bf16", seed=5)
 
 
+@pytest.mark.parametrize("N", [8192, 8200])
 @pytest.mark.parametrize("pattern", ["ramp", "steps", "falling"])
-def test_rows64_moving_max(attn, pattern):
+def test_rows64_moving_max(attn, pattern, N):
     """The rows64 kernel's rescale path: key norms that ramp up or double
     every 1024 keys along a long row (the running max moves by more than the
     kernel's threshold on later tiles and the accumulators are rescaled), and
     the reverse, on a shape that runs rows64, every head checked on sampled
-    rows."""
-    B, Hq, Hkv, N, d = 1, 16, 4, 8200, 128
+    rows.  N = 8192: a K/V head fits one XCD's L2, so alternate rounds of
+    workgroups stream the keys in reverse order (both orders in one launch);
+    N = 8200 has a partial last tile and keeps the forward order."""
+    B, Hq, Hkv, d = 1, 16, 4, 128
     _rows64_plan(attn, B, Hq, Hkv, N, d)
     _say(f"[parity] rows64 moving max {pattern} {B},{Hq},{Hkv},{N},{d}")
-    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=8200)
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=N)
     j = torch.arange(N, dtype=torch.float32)
     if pattern == "ramp":
         f = 1.0 + j / 512.0
