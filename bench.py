@@ -209,13 +209,94 @@ def mfma_ceiling(step_zero, stream, flops, steps: int):
     b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
     c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
     with torch.cuda.stream(stream):
-        _, gemm_ms, _, _ = time_launches(lambda: torch.matmul(a, b, out=c), stream, 20, 3)
-        _, zero_ms, _, _ = time_launches(step_zero, stream, max(5, steps // 2), 3)
+        gemm_ms, pw_gemm = sustained(lambda: torch.matmul(a, b, out=c), stream)
+        zero_ms, pw_zero = sustained(step_zero, stream)
     gemm = 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12
     del a, b, c
     return {"gemm": "torch.matmul bf16 8192x8192x8192, N(0,1) inputs", "gemm_tflops": round(gemm, 1),
-            "gemm_frac_of_peak": round(gemm / acc.PEAK_BF16_TFLOPS, 4),
-            "attn_zero_inputs_tflops": round(flops / (zero_ms * 1e-3) / 1e12, 1)}
+            "gemm_frac_of_peak": round(gemm / acc.PEAK_BF16_TFLOPS, 4), "gemm_power_clock": pw_gemm,
+            "attn_zero_inputs_tflops": round(flops / (zero_ms * 1e-3) / 1e12, 1),
+            "attn_zero_inputs_power_clock": pw_zero}
+
+
+def sustained(fn, stream, secs: float = 1.2):
+    """`fn` launched back to back for `secs` seconds with power and clock
+    sampled meanwhile (the device's metrics lag by tens of milliseconds, so
+    the summary keeps the later samples); returns (mean ms per launch over
+    the last half, the power / clock summary)."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    with PowerSampler() as pw:
+        t0 = time.perf_counter()
+        half = None
+        n = 0
+        while True:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+                el = time.perf_counter() - t0
+                if half is None and el >= secs / 2:
+                    half = (n, torch.cuda.Event(enable_timing=True))
+                    half[1].record(stream)
+                if el >= secs:
+                    break
+        end = torch.cuda.Event(enable_timing=True)
+        end.record(stream)
+        torch.cuda.synchronize()
+    ms = half[1].elapsed_time(end) / (n - half[0])
+    return ms, pw.summary()
+
+
+class PowerSampler:
+    """Socket power and graphics clock of GPU 0 (amdsmi), sampled every few
+    milliseconds while the `with` block runs; summary() gives their means
+    over the later half of the samples (or None without amdsmi)."""
+
+    def __init__(self, period_s: float = 0.005):
+        self.period = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+        self._h = None
+
+    def __enter__(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._amdsmi = amdsmi
+        except Exception:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+                    self.samples.append((float(m["current_socket_power"]), float(m["current_gfxclk"])))
+                except Exception:
+                    pass
+                time.sleep(self.period)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        s = self.samples[len(self.samples) // 2:]
+        if not s:
+            return None
+        return {"socket_power_w": round(sum(x for x, _ in s) / len(s), 1),
+                "gfxclk_mhz": round(sum(y for _, y in s) / len(s), 1), "samples": len(s)}
 
 
 def main():
@@ -242,6 +323,8 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="time the 8-bit entry point (attn_fwd_fp8) on the workload's shape: "
                          "E4M3 codes of seeded N(0,1) values with per-tensor scales")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the second of sustained launches that samples power and clock")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the library-GEMM / zero-input context measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -302,6 +385,9 @@ def main():
     with torch.cuda.stream(stream):
         n_warm, warm_ms = warm_up(step, args.warmup, args.min_warmup_ms)
         ms_step, ev_mean, ev_min, ev_med = time_launches(step, stream, args.steps, 0)
+        # the clock and power the kernel runs at, sampled over a further second
+        # of back-to-back launches (the timed steps may be too short to sample)
+        sus_ms, power = sustained(step, stream) if not args.no_power else (None, None)
     n_cu, n_xcd, l2_bytes = attn.attn_device_info()
     kernel = ("attn_fwd_f32_kernel" if w.dtype != "bf16" else
               "attn_fwd_fp8_kernel" if fp8 else
@@ -328,7 +414,10 @@ def main():
                 "hbm_gbps": (round(traffic / (ev_mean * 1e-3) / 1e9, 1) if traffic else None),
                 "hbm_frac": (round(traffic / (ev_mean * 1e-3) / 1e9 / acc.PEAK_HBM_GBPS, 4)
                              if traffic else None),
-                "device": {"compute_units": n_cu, "xcds": n_xcd, "l2_bytes": l2_bytes}}
+                "device": {"compute_units": n_cu, "xcds": n_xcd, "l2_bytes": l2_bytes},
+                # the clock the kernel runs at (the peak assumes 2.4 GHz)
+                "power_clock": (dict(power or {}, sustained_tflops=round(flops / (sus_ms * 1e-3) / 1e12, 1))
+                                if sus_ms else None)}
 
     materialized = None
     sp_bytes = w.B * w.Hq * w.N * w.N * (4 + w.elem_bytes)
