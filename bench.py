@@ -97,6 +97,28 @@ def materialized_traffic_from_profiles(workload: str, profiles_dir: str | None =
     return rec["hbm_read_bytes_per_launch"], rec["hbm_write_bytes_per_launch"]
 
 
+# the sources of the backward's kernels (row dot, dK/dV, dQ)
+BACKWARD_SOURCES = ["exact_io_aware_73_amd/csrc/attn_bwd.hip", "exact_io_aware_73_amd/csrc/kernels.hpp"]
+
+
+def backward_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in BACKWARD_SOURCES + _COMMON_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def backward_traffic_from_profiles(workload: str, profiles_dir: str | None = None):
+    """(read, write) bytes per call of the backward (its kernels summed) from
+    the committed counter summary, or None."""
+    rec = _counters(os.path.join(profiles_dir or os.path.join(ROOT, "profiles"),
+                                 f"attn_bwd_{workload}_counters.json"), backward_source_hash())
+    if rec is None:
+        return None
+    return rec["hbm_read_bytes_per_launch"], rec["hbm_write_bytes_per_launch"]
+
+
 def warm_up(fn, warmup: int, min_ms: float):
     """`warmup` launches, then more until at least `min_ms` of wall time has
     been spent launching: the GPU runs its first tens of milliseconds of work
@@ -468,8 +490,18 @@ def main():
             _, b_ms, _, _ = time_launches(bstep, stream, max(5, args.steps // 2), 3)
         # the usual accounting: 5 N x N x d products = 2.5x the forward's FLOPs
         # (the kernels run 7: S and dP are recomputed in both passes)
-        backward = {"ms": round(b_ms, 4), "tflops": round(2.5 * flops / (b_ms * 1e-3) / 1e12, 2),
-                    "flops": "2.5 x forward (5 products)", "executed_flops": "3.5 x forward",
+        b_tflops = 2.5 * flops / (b_ms * 1e-3) / 1e12
+        b_min = acc.bwd_min_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.elem_bytes)
+        b_meas = backward_traffic_from_profiles(w.name)
+        b_bytes = sum(b_meas) if b_meas else None
+        backward = {"ms": round(b_ms, 4), "tflops": round(b_tflops, 2),
+                    "frac": round(b_tflops / peak, 4),
+                    "flops": "2.5 x forward (5 products)",
+                    "executed_flops": "3.5 x forward" if w.d == 64 else "4 x forward",
+                    "min_bytes": b_min, "measured_bytes": b_bytes,
+                    "measured_read_write": list(b_meas) if b_meas else None,
+                    "measured_vs_min": round(b_bytes / b_min, 2) if b_bytes else None,
+                    "hbm_gbps": round(b_bytes / (b_ms * 1e-3) / 1e9, 1) if b_bytes else None,
                     "fwd_plus_bwd_ms": round(b_ms + ev_mean, 4)}
         del dout, o_f, lse_f, dq, dk, dv, ws_b
 

@@ -31,6 +31,13 @@ def min_bytes(B: int, Hq: int, Hkv: int, N: int, d: int, elem: int) -> int:
     return elem * (2 * B * Hq * N * d + 2 * B * Hkv * N * d)
 
 
+def bwd_min_bytes(B: int, Hq: int, Hkv: int, N: int, d: int, elem: int) -> int:
+    """The backward's least traffic: Q, K, V, O, dO and the fp32 lse read
+    once, dQ, dK, dV written once."""
+    return elem * (3 * B * Hq * N * d + 2 * B * Hkv * N * d) + 4 * B * Hq * N \
+        + elem * (B * Hq * N * d + 2 * B * Hkv * N * d)
+
+
 def lse_bytes(B: int, Hq: int, N: int) -> int:
     """The fp32 log-sum-exp output, B*Hq*N values."""
     return 4 * B * Hq * N

@@ -3,11 +3,13 @@ from __future__ import annotations
 
 import csv
 import json
+import os
 
 import pytest
 
 from exact_io_aware_73_amd import profiling
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TRACE_FIELDS = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
 
 
@@ -113,3 +115,38 @@ def test_materialized_counters_match_their_own_sources(tmp_path):
     assert bench.materialized_traffic_from_profiles(w, str(tmp_path)) == (7, 5)
     path.write_text(json.dumps(dict(rec, kernel_source_sha="stale")))
     assert bench.materialized_traffic_from_profiles(w, str(tmp_path)) is None
+
+
+def test_backward_counters_match_their_own_sources(tmp_path):
+    import bench
+
+    w = "long_b4_h32_n4096_d128"
+    rec = {"kernel_source_sha": bench.backward_source_hash(),
+           "hbm_read_bytes_per_launch": 11, "hbm_write_bytes_per_launch": 3}
+    path = tmp_path / f"attn_bwd_{w}_counters.json"
+    path.write_text(json.dumps(rec))
+    assert bench.backward_traffic_from_profiles(w, str(tmp_path)) == (11, 3)
+    path.write_text(json.dumps(dict(rec, kernel_source_sha="stale")))
+    assert bench.backward_traffic_from_profiles(w, str(tmp_path)) is None
+    assert bench.backward_source_hash() != bench.materialized_source_hash()
+
+
+def test_committed_backward_counters_are_current():
+    # every committed backward byte count was taken on the backward's current sources
+    import glob
+    import bench
+
+    paths = glob.glob(os.path.join(ROOT, "profiles", "attn_bwd_*_counters.json"))
+    assert paths
+    for p in paths:
+        rec = json.load(open(p))
+        assert rec["kernel_source_sha"] == bench.backward_source_hash(), p
+
+
+def test_backward_minimum_bytes():
+    from exact_io_aware_73_amd import accounting as acc
+
+    # one head, N = 1, d = 1: Q K V O dO read (5 x 2 bytes), lse (4), dQ dK dV (3 x 2)
+    assert acc.bwd_min_bytes(1, 1, 1, 1, 1, 2) == 10 + 4 + 6
+    # GQA 4:1: the K/V-sized tensors (K, V, dK, dV) scale with Hkv, the rest with Hq
+    assert acc.bwd_min_bytes(1, 4, 1, 8, 2, 2) == 2 * (4 * 4 * 8 * 2 + 4 * 1 * 8 * 2) + 4 * 4 * 8
