@@ -440,6 +440,13 @@ def main():
                 # the clock the kernel runs at (the peak assumes 2.4 GHz)
                 "power_clock": (dict(power or {}, sustained_tflops=round(flops / (sus_ms * 1e-3) / 1e12, 1))
                                 if sus_ms else None)}
+    if w.dtype == "bf16" and not fp8 and w.d == 128 and w.N >= 4096:
+        # the stated goals at N >= 4096, d = 128: half the bf16 peak, and at
+        # most 1.5x the Q/K/V/O bytes
+        roofline["targets"] = {
+            "frac_at_least": 0.5, "frac_met": achieved / peak >= 0.5,
+            "traffic_vs_min_at_most": 1.5,
+            "traffic_met": (traffic / minb <= 1.5) if traffic else None}
 
     materialized = None
     sp_bytes = w.B * w.Hq * w.N * w.N * (4 + w.elem_bytes)
