@@ -163,6 +163,10 @@ struct WaveState {
   int voff8[D == 128 ? 1 : G::kDB];  // the same for rows +8..11 (d = 64 only, see hi_off)
   int dvoff[G::kDma];              // byte offsets of this lane's direct loads within a tile
   int rev_last;                    // > 0: keys run in reverse order; the first key of the last tile
+  const char* kp;                  // byte address of the next K tile to load
+  const char* vp;                  // the same for V
+  int kleft, vleft;                // keys from the first key of that tile to the end
+  int dleft;                       // change of kleft / vleft per tile (-kBc, or kBc in reverse)
 };
 
 // Byte offset of the transposing V read of rows +8..11 for d block db.  For
@@ -174,31 +178,25 @@ __device__ __forceinline__ int hi_off(const WaveState<D>& w, int db) {
   return w.voff8[db];
 }
 
-// The tile loads: keys [j0, j0 + kBc) of one K or V head into one LDS slot.
-// The buffer covers only rows j0 .. N-1, so rows past N read as zeros and
-// nothing is read out of bounds (tiles past the end read nothing at all).
-// Issued as inline assembly: the compiler then does not see an LDS write
-// in flight and does not stall the LDS reads of the other slots behind it;
-// the step's own vmcnt wait and barrier order these loads against readers.
+// The tile loads: the next tile of one stream (K or V) in this wave's key
+// order into one LDS slot.  Each stream keeps the byte address of its next
+// tile and the keys from that tile's first key to the end of the range
+// ("left"), moved by one tile per load (backwards in reverse order).  The
+// buffer covers only the tile's rows that exist, so rows past the end read
+// as zeros and a tile outside the range (left <= 0, or left > N once a
+// reverse-order wave has passed the first key) reads nothing; every operand
+// of the buffer resource is wave-uniform (SGPRs).  Issued as inline
+// assembly: the compiler then does not see an LDS write in flight and does
+// not stall the LDS reads of the other slots behind it; the step's own
+// vmcnt wait and barrier order these loads against readers.
 template <int D>
-__device__ __forceinline__ void dma_tile_at(const int* dvoff, const __bf16* head, int j0, int N,
-                                            uint32_t lds_byte, int wave);
-// Tile j0 / kBc of the key order this wave runs: in reverse order the tiles
-// are taken from the end, and tiles past the last still read nothing.
-template <int D>
-__device__ __forceinline__ void dma_tile(const WaveState<D>& w, const __bf16* head, int j0, int N,
-                                         uint32_t lds_byte, int wave) {
-  if (w.rev_last > 0) j0 = j0 > w.rev_last ? N : w.rev_last - j0;
-  dma_tile_at<D>(w.dvoff, head, j0, N, lds_byte, wave);
-}
-template <int D>
-__device__ __forceinline__ void dma_tile_at(const int* dvoff, const __bf16* head, int j0, int N,
-                                            uint32_t lds_byte, int wave) {
+__device__ __forceinline__ void dma_next(const int* dvoff, const char*& ptr, int& left, int dleft,
+                                         int N, uint32_t lds_byte, int wave) {
   using G = FGeo<D>;
-  // every operand of the buffer resource is wave-uniform (SGPRs)
-  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(N - j0, kBc)));
+  // 0 < left <= N, as one unsigned compare
+  const int rows = (uint32_t)(left - 1) < (uint32_t)N ? (left < kBc ? left : kBc) : 0;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<__bf16*>(head) + (int64_t)min(j0, N) * D, (short)0, rows * D * 2, 0x00020000);
+      const_cast<char*>(ptr), (short)0, rows * D * 2, 0x00020000);
 #pragma unroll
   for (int i = 0; i < G::kDma; ++i) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(
@@ -206,6 +204,8 @@ __device__ __forceinline__ void dma_tile_at(const int* dvoff, const __bf16* head
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  ::"s"(dst), "v"(dvoff[i]), "s"(rs) : "memory");
   }
+  ptr -= (int64_t)dleft * (D * 2);
+  left += dleft;
 }
 
 __device__ __forceinline__ bf16x8 lds_k(uint32_t base, int off) {
@@ -223,9 +223,11 @@ __device__ __forceinline__ bf16x8 lds_vt(uint32_t base, int off, int off8) {
 // ---------------------------------------------------------------------------
 // The softmax of one tile as a list of small tasks, run in order and spread
 // over the MFMA slots of a step by their cost.
-//   tasks 0 .. 17   : row max, 9 per query block
-//   task  18        : move the running max if needed; alpha; l *= alpha
-//   tasks 19 .. 34  : 2 weights each: fma, exp2, round to bf16, add to l
+//   tasks 0 .. 17   : row max, 9 per query block; the ninth tests the lane's
+//                     half-row max against m + kRescaleLog2 (a ballot)
+//   task  18        : if any lane's test fired (a wave-uniform branch): the
+//                     max over both half-rows, the new m, alpha, l *= alpha
+//   tasks 19 .. 34  : 2 weights each: fma, exp2, add to l, round to bf16
 //   task  35        : fold the partial sums into l
 constexpr int kMaxTasks = 9;
 constexpr int kTasks = 2 * kMaxTasks + 1 + 16 + 1;
@@ -264,6 +266,7 @@ struct SoftmaxScratch {
   float mx[kQB][7];
   float ext[kQB];
   float alpha[kQB];
+  uint64_t hit[kQB];
   float ls[kQB][2];
   bool need;
 };
@@ -290,19 +293,21 @@ __device__ __forceinline__ void softmax_task(int t, WaveState<D>& w, SoftmaxScra
     } else if (i == 7) {
       sc.mx[qb][5] = ext2<kNeg>(sc.mx[qb][5], sc.mx[qb][6]);
     } else {
-      sc.ext[qb] = xhalf_ext<kNeg>(sc.mx[qb][5]) * c_log2;   // the row's max of s * c_log2
+      sc.hit[qb] = __builtin_amdgcn_ballot_w64(
+          __builtin_fmaf(sc.mx[qb][5], c_log2, -w.m[qb]) > kRescaleLog2);
     }
   } else if (t == 2 * kMaxTasks) {
     // move the running max only when some row's max grows by > 2^kRescaleLog2
-    sc.need = __any((sc.ext[0] > w.m[0] + kRescaleLog2) || (sc.ext[1] > w.m[1] + kRescaleLog2));
+    sc.need = (sc.hit[0] | sc.hit[1]) != 0;
+    if (sc.need) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float m_new = sc.need ? __builtin_fmaxf(w.m[qb], sc.ext[qb]) : w.m[qb];
-      sc.alpha[qb] = exp2_fast(w.m[qb] - m_new);   // 0 on the first tile
-      w.m[qb] = m_new;
-      w.l[qb] *= sc.alpha[qb];
-      sc.ls[qb][0] = 0.0f;
-      sc.ls[qb][1] = 0.0f;
+      for (int qb = 0; qb < kQB; ++qb) {
+        sc.ext[qb] = xhalf_ext<kNeg>(sc.mx[qb][5]) * c_log2;   // the row's max of s * c_log2
+        const float m_new = __builtin_fmaxf(w.m[qb], sc.ext[qb]);
+        sc.alpha[qb] = exp2_fast(w.m[qb] - m_new);   // 0 on the first tile
+        w.m[qb] = m_new;
+        w.l[qb] *= sc.alpha[qb];
+      }
     }
   } else if (t < kTasks - 1) {
     const int kk = t - (2 * kMaxTasks + 1);   // 0 .. 15
@@ -316,14 +321,18 @@ __device__ __forceinline__ void softmax_task(int t, WaveState<D>& w, SoftmaxScra
       if (8 * (e0 >> 2) + 4 * hh + (e0 & 3) >= valid) p0 = 0.0f;
       if (8 * (e1 >> 2) + 4 * hh + (e1 & 3) >= valid) p1 = 0.0f;
     }
-    const uint32_t pk = pack_bf16x2(p0, p1);
-    // P^T slot (hh, e) of k-step s2 holds key 16 s2 + 8 (e / 4) + 4 hh + e % 4,
-    // i.e. elements 8 s2 .. 8 s2 + 7 of the S^T accumulator
-    w.p[kPar][qb][x / 4][x % 4] = pk;
     // l sums the fp32 weights: the bf16-rounded ones would cost lse about
     // half a bf16 ulp of relative error on short rows
-    sc.ls[qb][0] += p0;
-    sc.ls[qb][1] += p1;
+    if (x == 0) {
+      sc.ls[qb][0] = p0;
+      sc.ls[qb][1] = p1;
+    } else {
+      sc.ls[qb][0] += p0;
+      sc.ls[qb][1] += p1;
+    }
+    // P^T slot (hh, e) of k-step s2 holds key 16 s2 + 8 (e / 4) + 4 hh + e % 4,
+    // i.e. elements 8 s2 .. 8 s2 + 7 of the S^T accumulator
+    w.p[kPar][qb][x / 4][x % 4] = pack_bf16x2(p0, p1);
   } else {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) w.l[qb] += sc.ls[qb][0] + sc.ls[qb][1];
@@ -341,9 +350,8 @@ __device__ __forceinline__ void softmax_task(int t, WaveState<D>& w, SoftmaxScra
 //   * the O rescale of tile j (after the P V of tile j - 1),
 // then waits for K tile j + 2 and V tile j (read by step j + 1) and syncs.
 template <int D, bool kNeg, int kJ4, bool kQK, bool kPV, bool kMask>
-__device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, const __bf16* kh,
-                                     const __bf16* vh, int j, int N, float c_log2, int wave,
-                                     int hh, bool first) {
+__device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, int j, int N,
+                                     float c_log2, int wave, int hh, bool first) {
   using G = FGeo<D>;
   constexpr int kPar = kJ4 & 1;
   constexpr uint32_t kTileB = G::kTile * 2;
@@ -373,9 +381,9 @@ __device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, const __bf16
   if (kSlotsUsed > 0) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      if (u == kDmaK) dma_tile<D>(w, kh, (j + kSlots) * kBc, N, lds + kJ4 * kTileB, wave);
+      if (u == kDmaK) dma_next<D>(w.dvoff, w.kp, w.kleft, w.dleft, N, lds + kJ4 * kTileB, wave);
       if (u == kDmaV)
-        dma_tile<D>(w, vh, (j + kSlots - 2) * kBc, N,
+        dma_next<D>(w.dvoff, w.vp, w.vleft, w.dleft, N,
                     lds + (kSlots + (kJ4 + kSlots - 2) % kSlots) * kTileB, wave);
       if (u + kAhead < kU) {
         if (kQK) kf[u + kAhead] = lds_k(k_rd, w.koff[u + kAhead]);
@@ -403,8 +411,8 @@ __device__ __forceinline__ void step(WaveState<D>& w, uint32_t lds, const __bf16
       }
     }
   } else {
-    dma_tile<D>(w, kh, (j + kSlots) * kBc, N, lds + kJ4 * kTileB, wave);
-    dma_tile<D>(w, vh, (j + kSlots - 2) * kBc, N,
+    dma_next<D>(w.dvoff, w.kp, w.kleft, w.dleft, N, lds + kJ4 * kTileB, wave);
+    dma_next<D>(w.dvoff, w.vp, w.vleft, w.dleft, N,
                 lds + (kSlots + (kJ4 + kSlots - 2) % kSlots) * kTileB, wave);
 #pragma unroll
     for (int t = 0; t < kTasks; ++t) softmax_task<D, kNeg, kMask, kPar>(t, w, sc, c_log2, valid, hh);
@@ -451,26 +459,24 @@ __device__ __forceinline__ void pv_last(WaveState<D>& w, uint32_t lds) {
 }
 
 template <int D, bool kNeg, int kJ4, bool kMask>
-__device__ __forceinline__ void last_step(WaveState<D>& w, uint32_t lds, const __bf16* kh,
-                                          const __bf16* vh, int j, int N, float c_log2, int wave,
-                                          int hh, bool single) {
+__device__ __forceinline__ void last_step(WaveState<D>& w, uint32_t lds, int j, int N,
+                                          float c_log2, int wave, int hh, bool single) {
   if (single)
-    step<D, kNeg, kJ4, false, false, kMask>(w, lds, kh, vh, j, N, c_log2, wave, hh, true);
+    step<D, kNeg, kJ4, false, false, kMask>(w, lds, j, N, c_log2, wave, hh, true);
   else
-    step<D, kNeg, kJ4, false, true, kMask>(w, lds, kh, vh, j, N, c_log2, wave, hh, j == 0);
+    step<D, kNeg, kJ4, false, true, kMask>(w, lds, j, N, c_log2, wave, hh, j == 0);
   pv_last<D, kJ4>(w, lds);
 }
 
 // Middle steps j0 .. j0 + kSlots - 1 (j0 % kSlots == 1), stopping before
 // the last tile: every step's slots are compile-time constants.
 template <int D, bool kNeg, size_t... I>
-__device__ __forceinline__ void middle_round(WaveState<D>& w, uint32_t lds, const __bf16* kh,
-                                             const __bf16* vh, int j0, int n_tiles, int N,
-                                             float c_log2, int wave, int hh,
+__device__ __forceinline__ void middle_round(WaveState<D>& w, uint32_t lds, int j0,
+                                             int n_tiles, int N, float c_log2, int wave, int hh,
                                              std::index_sequence<I...>) {
   bool go = true;
   ((go = go && (j0 + (int)I < n_tiles - 1) &&
-         (step<D, kNeg, (int)((I + 1) % kSlots), true, true, false>(w, lds, kh, vh, j0 + (int)I, N,
+         (step<D, kNeg, (int)((I + 1) % kSlots), true, true, false>(w, lds, j0 + (int)I, N,
                                                                     c_log2, wave, hh, false),
           true)),
    ...);
@@ -478,11 +484,11 @@ __device__ __forceinline__ void middle_round(WaveState<D>& w, uint32_t lds, cons
 
 // The last step of tile jl, its slot picked from jl % kSlots at run time.
 template <int D, bool kNeg, bool kMask, size_t... I>
-__device__ __forceinline__ void last_round(WaveState<D>& w, uint32_t lds, const __bf16* kh,
-                                           const __bf16* vh, int jl, int N, float c_log2, int wave,
-                                           int hh, std::index_sequence<I...>) {
+__device__ __forceinline__ void last_round(WaveState<D>& w, uint32_t lds, int jl, int N,
+                                           float c_log2, int wave, int hh,
+                                           std::index_sequence<I...>) {
   ((jl % kSlots == (int)I
-        ? (last_step<D, kNeg, (int)I, kMask>(w, lds, kh, vh, jl, N, c_log2, wave, hh, false), 0)
+        ? (last_step<D, kNeg, (int)I, kMask>(w, lds, jl, N, c_log2, wave, hh, false), 0)
         : 0),
    ...);
 }
@@ -617,11 +623,20 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
 
   // ---- prologue: K tiles 0 .. S-1 and V tiles 0 .. S-3 in flight; S of tile 0
   constexpr uint32_t kTileB = G::kTile * 2;
+  {
+    const bool rev = w.rev_last > 0;
+    const int first = rev ? w.rev_last : 0;
+    w.kp = reinterpret_cast<const char*>(kh + (int64_t)first * D);
+    w.vp = reinterpret_cast<const char*>(vh + (int64_t)first * D);
+    w.kleft = w.vleft = ATTN_KEYS - first;
+    w.dleft = rev ? kBc : -kBc;
+  }
 #pragma unroll
-  for (int t = 0; t < kSlots; ++t) dma_tile<D>(w, kh, t * kBc, ATTN_KEYS, lds + t * kTileB, wave);
+  for (int t = 0; t < kSlots; ++t)
+    dma_next<D>(w.dvoff, w.kp, w.kleft, w.dleft, ATTN_KEYS, lds + t * kTileB, wave);
 #pragma unroll
   for (int t = 0; t < kSlots - 2; ++t)
-    dma_tile<D>(w, vh, t * kBc, ATTN_KEYS, lds + (kSlots + t) * kTileB, wave);
+    dma_next<D>(w.dvoff, w.vp, w.vleft, w.dleft, ATTN_KEYS, lds + (kSlots + t) * kTileB, wave);
   // K tiles 0 and 1 must have landed: S of tile 0 reads K slot 0 here and
   // step 0 reads K slot 1 (for S of tile 1) before its own wait; the other
   // 2 kSlots - 4 tiles may still be in flight
@@ -638,20 +653,20 @@ void attn_fwd_bf16_rows64_kernel(const __bf16* __restrict__ q, const __bf16* __r
 
   const bool tail = (ATTN_KEYS % kBc) != 0;
   if (n_tiles == 1) {
-    if (tail) last_step<D, kNeg, 0, true>(w, lds, kh, vh, 0, ATTN_KEYS, c_log2, wave, hh, true);
-    else last_step<D, kNeg, 0, false>(w, lds, kh, vh, 0, ATTN_KEYS, c_log2, wave, hh, true);
+    if (tail) last_step<D, kNeg, 0, true>(w, lds, 0, ATTN_KEYS, c_log2, wave, hh, true);
+    else last_step<D, kNeg, 0, false>(w, lds, 0, ATTN_KEYS, c_log2, wave, hh, true);
   } else {
-    step<D, kNeg, 0, true, false, false>(w, lds, kh, vh, 0, ATTN_KEYS, c_log2, wave, hh, true);
+    step<D, kNeg, 0, true, false, false>(w, lds, 0, ATTN_KEYS, c_log2, wave, hh, true);
     // middle steps 1 .. n_tiles - 2, unrolled by the ring size so every
     // slot index is a constant
     for (int j = 1; j < n_tiles - 1; j += kSlots)
-      middle_round<D, kNeg>(w, lds, kh, vh, j, n_tiles, ATTN_KEYS, c_log2, wave, hh,
+      middle_round<D, kNeg>(w, lds, j, n_tiles, ATTN_KEYS, c_log2, wave, hh,
                             std::make_index_sequence<kSlots>{});
     const int jl = n_tiles - 1;
     if (tail)
-      last_round<D, kNeg, true>(w, lds, kh, vh, jl, ATTN_KEYS, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
+      last_round<D, kNeg, true>(w, lds, jl, ATTN_KEYS, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
     else
-      last_round<D, kNeg, false>(w, lds, kh, vh, jl, ATTN_KEYS, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
+      last_round<D, kNeg, false>(w, lds, jl, ATTN_KEYS, c_log2, wave, hh, std::make_index_sequence<kSlots>{});
   }
   // loads past the last tile may still be writing LDS: drain before exit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
