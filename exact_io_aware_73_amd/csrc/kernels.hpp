@@ -43,17 +43,18 @@ uint64_t fwd_f32_grid(int B, int Hq, int N);
 //   rows64 -- two 32-row query blocks per wave sharing every K / V fragment
 //             read from LDS, software-pipelined across key tiles, 256 query
 //             rows per workgroup, one workgroup per CU (head dim 128).
-// Head dim 128 takes rows64 where the keys are long (N >= 8192) and its grid
-// has at least one workgroup per CU; elsewhere rows32, whose smaller
+// Head dim 128 takes rows64 where the keys are not short (N >= 1024) and its
+// grid has at least one workgroup per CU; elsewhere rows32, whose smaller
 // workgroups spread a small grid over every CU and hide the per-workgroup
-// start and end behind a second workgroup (measured: N = 200 GQA +24 %,
-// one head of 32768 rows +39 %, N = 4096 +2 %; N >= 8192 with a full grid
-// -2 ... -4 %).  n_cu is the device's compute-unit count (read from the HIP
-// runtime once per device).
+// start and end behind a second workgroup (measured, rows64 against rows32
+// with a full grid: N = 4096 +5 ... +6 %, 2048 +5 %, 1024 +2 %, 512 -6 %,
+// 256 -10 %; one head of 32768 rows, 128 workgroups, rows32 +39 %).  n_cu is
+// the device's compute-unit count (read from the HIP runtime once per
+// device).
 hipError_t launch_fwd_bf16_rows32(const FwdArgs& a);
 hipError_t launch_fwd_bf16_rows64(const FwdArgs& a);
 inline bool fwd_bf16_use_rows64(int B, int Hq, int Hkv, int N, int d, int n_cu) {
-  return d == 128 && N >= 8192 && fwd_bf16_rows64_grid(B, Hq, Hkv, N) >= (uint64_t)n_cu;
+  return d == 128 && N >= 1024 && fwd_bf16_rows64_grid(B, Hq, Hkv, N) >= (uint64_t)n_cu;
 }
 hipError_t launch_fwd_f32(const FwdArgs& a);
 

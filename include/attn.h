@@ -268,7 +268,7 @@ ATTN_API int attn_device_info(int* n_cu, int* n_xcd, int* l2_bytes);
 /*
  * attn_fwd_plan -- which kernel attn_fwd launches for these sizes on the
  * calling thread's current device: ATTN_KERNEL_ROWS64 for head dim 128 with
- * N >= 8192 and at least one 256-row workgroup per compute unit, else
+ * N >= 1024 and at least one 256-row workgroup per compute unit, else
  * ATTN_KERNEL_ROWS32.  The same argument checks as attn_fwd (pointers
  * aside); *kernel (host pointer, not NULL) is written only on ATTN_OK.
  */

@@ -94,7 +94,7 @@ def test_fwd_past_2_31_elements(attn, d):
 
 
 def test_rows64_past_2_31_elements(attn):
-    """The rows64 kernel (head dim 128, N >= 8192, a full grid) on tensors
+    """The rows64 kernel (head dim 128, N >= 1024, a full grid) on tensors
     past 2^31 elements: 2 x 1025 heads of 8192 rows, the first and last
     random and checked on sampled rows, every other head zero."""
     B, H, Nl, d = 2, 1025, 8192, 128

@@ -383,15 +383,16 @@ def _rows64_plan(attn, B, Hq, Hkv, N, d):
 
 def test_kernel_plan_by_shape(attn):
     """Which kernel each bf16 shape runs, asked of the library: rows64 where
-    N >= 8192 and the 256-row grid has a workgroup per compute unit."""
+    head dim 128, N >= 1024 and the 256-row grid has a workgroup per compute
+    unit."""
     n_cu, n_xcd, l2 = attn.attn_device_info()
     _say(f"[parity] device: {n_cu} compute units, {n_xcd} XCDs, L2 {l2} bytes")
     assert n_cu >= 1 and n_xcd >= 1
     R32, R64 = attn.ATTN_KERNEL_ROWS32, attn.ATTN_KERNEL_ROWS64
-    want = {"gpt2_medium_b64_h16_n1024_d64": R32, "long_b4_h32_n4096_d128": R32,
-            "gqa_short_b64_hq32_hkv4_n200_d128": R32}
+    want = {"gpt2_medium_b64_h16_n1024_d64": R32, "gqa_short_b64_hq32_hkv4_n200_d128": R32}
     if n_cu <= 256:
-        want.update({"gqa_b2_hq32_hkv8_n8192_d128": R64, "long_context_b1_h8_n32768_d128": R64})
+        want.update({"gqa_b2_hq32_hkv8_n8192_d128": R64, "long_context_b1_h8_n32768_d128": R64,
+                     "long_b4_h32_n4096_d128": R64})
     if n_cu > 128:
         want["one_head_b1_h1_n32768_d128"] = R32     # 128 workgroups of 256 rows
     for name, kern in want.items():
@@ -401,10 +402,13 @@ def test_kernel_plan_by_shape(attn):
     rows_for = lambda g_rows: -(-g_rows // 256)        # 256-row workgroups of one group
     hkv = -(-n_cu // rows_for(4 * 8192))                 # just enough groups to fill the CUs
     assert attn.attn_fwd_plan(1, 4 * hkv, hkv, 8192, 128) == R64
-    assert attn.attn_fwd_plan(1, 4 * hkv, hkv, 8191, 128) == R32
     assert attn.attn_fwd_plan(1, 4 * hkv, hkv, 8192, 64) == R32
     if hkv > 1:
         assert attn.attn_fwd_plan(1, 4 * (hkv - 1), hkv - 1, 8192, 128) == R32
+    h = -(-n_cu // rows_for(1024))                        # heads of 1024 rows filling the CUs
+    assert attn.attn_fwd_plan(1, h, h, 1024, 128) == R64
+    assert attn.attn_fwd_plan(1, h, h, 1023, 128) == R32
+    assert attn.attn_fwd_plan(1, 2 * h, 2 * h, 1023, 128) == R32
 
 
 @pytest.mark.parametrize("scale", [1 / math.sqrt(128), -0.05, 0.0])
@@ -429,7 +433,7 @@ def test_rows64_reversed_rounds(attn, scale):
 
 @pytest.mark.parametrize("scale", [1 / math.sqrt(128), -0.05])
 def test_rows64_long_ragged(attn, scale):
-    """Head dim 128 with N >= 8192 and a grid of at least one workgroup per CU
+    """Head dim 128 with N >= 1024 and a grid of at least one workgroup per CU
     runs the rows64 kernel (shorter keys or smaller grids run rows32): a
     ragged last key tile and a GQA group, sampled rows against the oracle."""
     B, Hq, Hkv, N, d = 1, 16, 4, 8197, 128
@@ -439,6 +443,23 @@ def test_rows64_long_ragged(attn, scale):
     o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), scale)
     torch.cuda.synchronize()
     check_sampled(q, k, v, o.cpu(), lse.cpu(), scale, "bf16", seed=5)
+
+
+@pytest.mark.parametrize("N", [1024, 1500])
+def test_rows64_short_keys(attn, N):
+    """The shortest keys rows64 takes (N >= 1024, a full grid of GQA groups):
+    whole and ragged last tiles, every head checked on sampled rows."""
+    n_cu = attn.attn_device_info()[0]
+    hkv = max(4, -(-n_cu // (-(-4 * N // 256))))
+    B, Hq, Hkv, d = 1, 4 * hkv, hkv, 128
+    _rows64_plan(attn, B, Hq, Hkv, N, d)
+    _say(f"[parity] rows64 short keys {B},{Hq},{Hkv},{N},{d}")
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=N + 3)
+    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    check_sampled(q, k, v, o, lse, 1.0 / math.sqrt(d), "bf16", seed=3)
+    check_every_head(q, k, v, o, lse, 1.0 / math.sqrt(d), "bf16", seed=3, n_rows=8)
 
 
 @pytest.mark.parametrize("N", [8192, 8200])
