@@ -297,8 +297,11 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   commit(0);
   __syncthreads();
 
-  for (int t = 0; t < n_steps; ++t) {
-    const uint32_t stage = lds + (uint32_t)(t & 1) * kStageB;
+  // one query step in LDS stage `st` (a compile-time constant: the loop
+  // below runs two steps per trip, so every LDS read has a fixed offset)
+  auto q_step = [&](const int t, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    const uint32_t stage = lds + (uint32_t)st * kStageB;
     const uint32_t qtile = stage, dotile = stage + kTileB;
     const uint32_t lse_s = stage + 2 * kTileB, d_s = lse_s + kTRows * 4;
     if (t + 1 < n_steps) issue(t + 1);
@@ -404,6 +407,10 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     wait_vm();
     if (t + 1 < n_steps) commit(t + 1);
     __syncthreads();
+  };
+  for (int t = 0; t < n_steps; t += 2) {
+    q_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_steps) q_step(t + 1, std::integral_constant<int, 1>{});
   }
 
   if (krow < N) {
@@ -467,16 +474,16 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
   __syncthreads();
 
   const int n_kt = (N + kTRows - 1) / kTRows;
-  for (int jt = 0; jt < n_kt; ++jt) {
-    const uint32_t stage = lds + (uint32_t)(jt & 1) * kStageB;
-    const uint32_t ktile = stage, vtile = stage + kTileB;
+  // one key tile in LDS stage `st` (a compile-time constant: the loop below
+  // runs two tiles per trip, so every LDS read has a fixed offset)
+  auto key_tile = [&](const int jt, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    const uint32_t ktile = lds + (uint32_t)st * kStageB, vtile = ktile + kTileB;
     if (jt + 1 < n_kt) {
-      const uint32_t nxt = lds + (uint32_t)((jt + 1) & 1) * kStageB;
+      const uint32_t nxt = lds + (uint32_t)(1 - st) * kStageB;
       dma_tile<D>(kh, (jt + 1) * kTRows, N, nxt, wave, off.dvoff);
       dma_tile<D>(vh, (jt + 1) * kTRows, N, nxt + kTileB, wave, off.dvoff);
     }
-    const int j0 = jt * kTRows;
-    const bool tail = j0 + kTRows > N;
 #pragma unroll
     for (int kb = 0; kb < kTRows / 32; ++kb) {
       // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
@@ -488,12 +495,15 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         sacc = mfma32x32x16(ka, qf[s], sacc);
         pacc = mfma32x32x16(va, df[s], pacc);
       }
-      // element e: key j0 + kb*32 + 8 (e / 4) + 4 hh + e % 4
+      // Keys past N need no mask: their K and V rows read as zeros, so their
+      // dS meets a zero row of K in dQ += K^T dS^T.  Their weight 2^-lse2
+      // only has to stay finite, which the clamp of every weight to [0, 1]
+      // (the exponent's output modifier; a weight of a key that exists is
+      // at most 1 up to rounding) guarantees.
       float ds[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float pe = exp2_fast(__builtin_fmaf(sacc[e], c_log2, -lse2));
-        if (tail && j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3) >= N) pe = 0.0f;
+        const float pe = __builtin_amdgcn_fmed3f(exp2_fast(__builtin_fmaf(sacc[e], c_log2, -lse2)), 0.0f, 1.0f);
         ds[e] = pe * (pacc[e] - dd);
       }
       // dQ^T += K^T dS^T over the two 16-key k-steps
@@ -510,6 +520,10 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     }
     wait_vm();
     __syncthreads();
+  };
+  for (int jt = 0; jt < n_kt; jt += 2) {
+    key_tile(jt, std::integral_constant<int, 0>{});
+    if (jt + 1 < n_kt) key_tile(jt + 1, std::integral_constant<int, 1>{});
   }
 
   if (qvalid) store_rowT<D>(dqacc, dq + (head_q + qrow) * D, scale, hh);
