@@ -73,6 +73,40 @@ def test_bwd_scales(attn, scale):
     _check(attn, q, k, v, do, scale, f"scale {scale}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_very_negative_logits_ragged(attn, d):
+    """Every score near -150 (lse the same), N = 100 (a partial last key
+    tile): a key past N would weigh exp(-lse) = e^150, past fp32 range, in
+    the dQ kernel, which takes such keys without a mask (their K rows are
+    zero); the clamped weight keeps them finite, so no inf or NaN reaches dQ."""
+    N = 100
+    q, k, v, do = _inputs(1, 2, 1, N, d, 400 + d)
+    a = math.sqrt(150.0 / d)
+    q = (a + 0.05 * q.float()).to(torch.bfloat16)
+    k = (-a + 0.05 * k.float()).to(torch.bfloat16)
+    got = _grads(attn, q, k, v, do, 1.0)
+    assert all(torch.isfinite(g.float()).all() for g in got)
+    ref = oracle.attention_bwd_ref(workloads.to_f64(q), workloads.to_f64(k), workloads.to_f64(v),
+                                   workloads.to_f64(do), 1.0)
+    # dV has no cancellation: the usual bound
+    err = float(np.max(np.abs(workloads.to_f64(got[2]) - ref[2])))
+    assert err <= 1e-2 * float(np.max(np.abs(ref[2]))) + 1e-4, ("dv", err)
+    # dQ = dS K and dK = dS^T Q sum terms that nearly cancel (K and Q share a
+    # large common part here), so the bf16 rounding of P and dS (2^-9 each)
+    # is bounded per entry by the sum of the terms' magnitudes, not by the result
+    Q, K, V, dO = (workloads.to_f64(x)[0] for x in (q, k, v, do))
+    K, V = np.repeat(K, 2, axis=0), np.repeat(V, 2, axis=0)
+    S = Q @ K.transpose(0, 2, 1)
+    P = np.exp(S - S.max(-1, keepdims=True))
+    P /= P.sum(-1, keepdims=True)
+    dS = P * (dO @ V.transpose(0, 2, 1) - (dO * (P @ V)).sum(-1, keepdims=True))
+    bound_q = 2.0 ** -7 * (np.abs(dS) @ np.abs(K)) + 1e-4
+    bound_k = 2.0 ** -7 * np.abs(dS).transpose(0, 2, 1) @ np.abs(Q)
+    bound_k = bound_k.reshape(1, 2, N, d).sum(1) + 1e-4
+    assert np.all(np.abs(workloads.to_f64(got[0])[0] - ref[0][0]) <= bound_q), "dq"
+    assert np.all(np.abs(workloads.to_f64(got[1])[0] - ref[1][0]) <= bound_k[0]), "dk"
+
+
 def test_bwd_longer_gqa(attn):
     q, k, v, do = _inputs(1, 4, 1, 1024, 128, 91)
     _check(attn, q, k, v, do, 1 / math.sqrt(128), "N=1024 GQA 4:1")
