@@ -23,7 +23,9 @@
 //    limits that layout).
 //  * In the S^T output layout a lane owns ONE query (column l % 32) and 16
 //    of the 32 keys, so the row max / row sum are in-lane reductions plus
-//    one v_permlane32_swap with the other half-wave.
+//    one v_permlane32_swap with the other half-wave.  The swap is needed
+//    only when the running max moves: whether it must is a ballot of each
+//    half-row's own max.
 //  * O^T = V^T P^T on the same MFMA: P^T comes straight from the S^T
 //    accumulator registers (rounded to bf16); the V^T operand is read from
 //    the row-major V tile with ds_read_b64_tr_b16, which hands each lane
@@ -35,7 +37,10 @@
 //    of tile j.  The step is scheduled by hand: every MFMA is followed by a
 //    slice of the softmax work, the slices balanced by their cycle cost, and
 //    a scheduling fence keeps that order, so one wave keeps the matrix core
-//    and the vector ALU busy at the same time.
+//    and the vector ALU busy at the same time.  With one wave per SIMD every
+//    instruction it issues between two MFMAs costs time (~4 cycles each,
+//    measured), so the step carries as few as it can: the rare rescale in a
+//    wave-uniform branch, tile-load addresses advanced rather than rebuilt.
 //  * K and V tiles go global -> LDS directly (buffer_load ... lds, the rows
 //    past N read as zeros by the buffer's range check) into a ring of four
 //    slots each, three tiles ahead of their use; one barrier per step.  The
