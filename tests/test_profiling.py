@@ -150,3 +150,20 @@ def test_backward_minimum_bytes():
     assert acc.bwd_min_bytes(1, 1, 1, 1, 1, 2) == 10 + 4 + 6
     # GQA 4:1: the K/V-sized tensors (K, V, dK, dV) scale with Hkv, the rest with Hq
     assert acc.bwd_min_bytes(1, 4, 1, 8, 2, 2) == 2 * (4 * 4 * 8 * 2 + 4 * 1 * 8 * 2) + 4 * 4 * 8
+
+
+def test_committed_forward_counters_are_current():
+    # every committed byte count of the fused and materialising paths was
+    # taken on the sources the kernel it describes is built from now
+    import glob
+    import bench
+
+    paths = glob.glob(os.path.join(ROOT, "profiles", "attn_fwd_*_counters.json"))
+    assert paths
+    for p in paths:
+        rec = json.load(open(p))
+        if "_materialized_" in os.path.basename(p):
+            want = bench.materialized_source_hash()
+        else:
+            want = bench.kernel_source_hash(rec["workload"])
+        assert rec["kernel_source_sha"] == want, p
