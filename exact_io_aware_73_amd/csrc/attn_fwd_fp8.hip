@@ -286,7 +286,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restric
 #pragma unroll
         for (int i = 0; i < w / 2; ++i)
           t[i] = kNegScale ? vmin(t[i], t[i + w / 2]) : vmax(t[i], t[i + w / 2]);
-      ext = kNegScale ? xhalf_min(t[0]) : xhalf_max(t[0]);
+      ext = t[0];
     } else {
       float e2 = kNegScale ? INFINITY : -INFINITY;
 #pragma unroll
@@ -296,11 +296,12 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restric
           const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
           if (key < N) e2 = kNegScale ? vmin(e2, sacc[kb][e]) : vmax(e2, sacc[kb][e]);
         }
-      ext = kNegScale ? xhalf_min(e2) : xhalf_max(e2);
+      ext = e2;
     }
-    ext *= c_log2;
 
-    if (__any(ext > m_run + kRescaleLog2)) {
+    // the test on each half-row's own max; both halves' max only on a move
+    if (__builtin_amdgcn_ballot_w64(__builtin_fmaf(ext, c_log2, -m_run) > kRescaleLog2) != 0) {
+      ext = (kNegScale ? xhalf_min(ext) : xhalf_max(ext)) * c_log2;
       const float m_new = fmaxf(m_run, ext);
       const float alpha = exp2_fast(m_run - m_new);   // 0 on the first tile
       m_run = m_new;
