@@ -536,3 +536,60 @@ def test_materialized_long_workload(attn):
         r = compare(workloads.to_f64(o[b, h, rows]), lse[b, h, rows].cpu().numpy(), O_ref, l_ref, "bf16")
         assert r["ok"], r
     del s, p
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes across both kernels and both key orders: head counts,
+# GQA ratios, ragged N on either side of the rows64 threshold, both signs of
+# scale; every head checked on a few rows, three heads on more
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.integers(1, 9))
+        B = int(rng.integers(1, 4))
+        N = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(900, 1200)),
+                            int(rng.integers(1500, 6000)), 4096, 8192]))
+        scale = float(rng.choice([1.0 / math.sqrt(d), -0.07, 0.3]))
+        shapes.append((B, g * hkv, hkv, N, d, scale, 1000 + i))
+    return shapes
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,scale,seed", _random_shapes(16, 20261203))
+def test_random_shapes(attn, B, Hq, Hkv, N, d, scale, seed):
+    _say(f"[parity] random shape {B},{Hq},{Hkv},{N},{d} scale={scale:.3f} "
+         f"plan={attn.attn_fwd_plan(B, Hq, Hkv, N, d)}")
+    q, k, v = workloads.random_inputs(B, Hq, Hkv, N, d, torch.bfloat16, seed=seed)
+    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    check_sampled(q, k, v, o, lse, scale, "bf16", seed=seed)
+    check_every_head(q, k, v, o, lse, scale, "bf16", seed=seed, n_rows=2)
+
+
+def _random_rows64_shapes(n, seed):
+    """Head dim 128, N >= 1024 and enough K/V groups to fill 256 compute units
+    with 256-row workgroups: the rows64 kernel, ragged and whole last tiles,
+    groups spanning one or several rounds (the reversed key order)."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        g = int(rng.choice([1, 2, 4, 8]))
+        N = int(rng.choice([int(rng.integers(1024, 9000)), 32 * int(rng.integers(32, 300))]))
+        per_group = -(-g * N // 256)
+        groups = -(-256 // per_group) + int(rng.integers(0, 3))
+        B = 1 + int(rng.integers(0, 2))
+        hkv = -(-groups // B)
+        scale = float(rng.choice([1.0 / math.sqrt(128), -0.07, 0.3]))
+        shapes.append((B, g * hkv, hkv, N, 128, scale, 2000 + i))
+    return shapes
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,scale,seed", _random_rows64_shapes(8, 1203))
+def test_random_rows64_shapes(attn, B, Hq, Hkv, N, d, scale, seed):
+    n_cu = attn.attn_device_info()[0]
+    if n_cu <= 256:
+        _rows64_plan(attn, B, Hq, Hkv, N, d)
+    test_random_shapes(attn, B, Hq, Hkv, N, d, scale, seed)
