@@ -496,7 +496,8 @@ def main():
         with torch.cuda.stream(stream):
             _, b_ms, _, _ = time_launches(bstep, stream, max(5, args.steps // 2), 3)
         # the usual accounting: 5 N x N x d products = 2.5x the forward's FLOPs
-        # (the kernels run 7: S and dP are recomputed in both passes)
+        # (the kernels run 7: S and dP are computed by both the dK/dV and
+        # the dQ kernel)
         b_tflops = 2.5 * flops / (b_ms * 1e-3) / 1e12
         b_min = acc.bwd_min_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.elem_bytes)
         b_meas = backward_traffic_from_profiles(w.name)
@@ -504,7 +505,7 @@ def main():
         backward = {"ms": round(b_ms, 4), "tflops": round(b_tflops, 2),
                     "frac": round(b_tflops / peak, 4),
                     "flops": "2.5 x forward (5 products)",
-                    "executed_flops": "3.5 x forward" if w.d == 64 else "4 x forward",
+                    "executed_flops": "3.5 x forward (7 products)",
                     "min_bytes": b_min, "measured_bytes": b_bytes,
                     "measured_read_write": list(b_meas) if b_meas else None,
                     "measured_vs_min": round(b_bytes / b_min, 2) if b_bytes else None,

@@ -17,7 +17,9 @@
 //   attn_bwd_dkdv    -- one workgroup per 128 keys of a K/V head: its K and V
 //                       rows stay in registers while the Q / dO tiles of every
 //                       query head of the group stream through LDS; dK and dV
-//                       accumulate in registers and are written once;
+//                       accumulate in registers and are written once (head
+//                       dim 64; at 128 attn_bwd_dkdv_rs splits each 32 keys'
+//                       work over two waves, below);
 //   attn_bwd_dq      -- one workgroup per 128 query rows: the K / V tiles of
 //                       the head stream through LDS (as in the forward) and dQ
 //                       accumulates in registers; no atomics anywhere.
@@ -215,13 +217,11 @@ void attn_bwd_rowdot_kernel(const __bf16* __restrict__ o, const __bf16* __restri
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per 128 keys of K/V head (b, kvh).  kOut picks the
-// outputs: both (0), dV only (1) or dK only (2).  At head dim 128 both at
-// once need 368 registers (one wave per SIMD, latency-bound); apart, the dV
-// pass (S and dV products, 180 registers) and the dK pass (S, dP and dK,
-// 240) each run two waves per SIMD.
-template <int D, int kOut>
-__global__ __launch_bounds__(kBThreads, D == 64 || kOut != 0 ? 2 : 1)
+// dK, dV at head dim 64: one workgroup per 128 keys of K/V head (b, kvh),
+// two workgroups (two waves per SIMD) per CU; each wave owns 32 keys and
+// runs all four products for them.
+template <int D>
+__global__ __launch_bounds__(kBThreads, 2)
 void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                           const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                           const float* __restrict__ lse, const float* __restrict__ dvec,
@@ -253,10 +253,10 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   const int64_t head_q = ((int64_t)b * Hkv + kvh) * (int64_t)n_qrows;
 
   const int krow = kt * kWgRows + wave * kWRows + l32;   // this lane's key (B operand column)
-  constexpr bool kDV = kOut != 2, kDK = kOut != 1;
+  static_assert(D == 64, "head dim 128 runs attn_bwd_dkdv_rs_kernel");
   bf16x8 kf[G::kKSteps], vf[G::kKSteps];
   load_rowfrags<D>(kf, k + head_kv * D, krow, N, hh);
-  if (kDK) load_rowfrags<D>(vf, v + head_kv * D, krow, N, hh);
+  load_rowfrags<D>(vf, v + head_kv * D, krow, N, hh);
 
   const TileOffsets<D> off = tile_offsets<D>(lane, wave);
   f32x16 dkacc[G::kDB], dvacc[G::kDB];
@@ -269,25 +269,28 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   const int n_steps = (n_qrows + kTRows - 1) / kTRows;   // 64-row query tiles of the group
 
   // Loads of step t into stage t & 1: the Q and dO tiles go global -> LDS
-  // directly; lse*log2e and D of the 64 rows come through registers (rows
-  // past the group's last get lse = +inf, so their weights are
-  // exp2(-inf) = 0, and D = 0).
+  // directly; lse and D of the 64 rows come through registers (rows past
+  // the group's last get lse = +inf, so their weights are exp2(-inf) = 0,
+  // and D = 0).  The row statistics are loaded before the tiles and scaled
+  // only when committed: a use right after the load would make the wave
+  // wait for every load in flight, the tile loads issued just before
+  // included (the wait counter counts them all, in order).
   float st_lse = 0.0f, st_d = 0.0f;
   auto issue = [&](int t) {
     const int q0 = t * kTRows;
     const uint32_t stage = lds + (uint32_t)(t & 1) * kStageB;
-    dma_tile<D>(q + head_q * D, q0, n_qrows, stage, wave, off.dvoff);
-    dma_tile<D>(dout + head_q * D, q0, n_qrows, stage + kTileB, wave, off.dvoff);
     if (tid < kTRows) {
       const int row = q0 + tid;
-      st_lse = row < n_qrows ? lse[head_q + row] * kLog2e : INFINITY;
+      st_lse = row < n_qrows ? lse[head_q + row] : INFINITY;
       st_d = row < n_qrows ? dvec[head_q + row] : 0.0f;
     }
+    dma_tile<D>(q + head_q * D, q0, n_qrows, stage, wave, off.dvoff);
+    dma_tile<D>(dout + head_q * D, q0, n_qrows, stage + kTileB, wave, off.dvoff);
   };
   auto commit = [&](int t) {   // after the loads of step t have landed
     if (tid < kTRows) {
       const uint32_t stage = lds + (uint32_t)(t & 1) * kStageB;
-      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + tid * 4) = st_lse;
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + tid * 4) = st_lse * kLog2e;
       *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + kTRows * 4 + tid * 4) = st_d;
     }
   };
@@ -306,101 +309,45 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     const uint32_t lse_s = stage + 2 * kTileB, d_s = lse_s + kTRows * 4;
     if (t + 1 < n_steps) issue(t + 1);
 
-    if constexpr (D == 128) {
-      // d = 128 (one wave per SIMD: the wave itself has to keep the matrix
-      // core busy): S = Q K^T and dP = dO V^T for both 32-query blocks first,
-      // so the products of block 1 overlap the weights of block 0 (7 % faster)
-      constexpr int kQB = kTRows / 32;
-      f32x16 sacc[kQB], pacc[kQB];
+    // block by block (two waves per SIMD: the other wave fills in)
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        sacc[qb] = f32x16{};
-        pacc[qb] = f32x16{};
+    for (int qb = 0; qb < kTRows / 32; ++qb) {
+      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-        for (int s = 0; s < G::kKSteps; ++s) {
-          const bf16x8 qa = lds_row(qtile + qb * 32 * D * 2, off.row[s]);
-          sacc[qb] = mfma32x32x16(qa, kf[s], sacc[qb]);
-          if (kDK) {
-            const bf16x8 da = lds_row(dotile + qb * 32 * D * 2, off.row[s]);
-            pacc[qb] = mfma32x32x16(da, vf[s], pacc[qb]);
-          }
+      for (int s = 0; s < G::kKSteps; ++s) {
+        const bf16x8 qa = lds_row(qtile + qb * 32 * D * 2, off.row[s]);
+        const bf16x8 da = lds_row(dotile + qb * 32 * D * 2, off.row[s]);
+        sacc = mfma32x32x16(qa, kf[s], sacc);
+        pacc = mfma32x32x16(da, vf[s], pacc);
+      }
+      // element 4 r + j: query qb*32 + 8 r + 4 hh + j
+      float p[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 l4 = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+        const f32x4 d4 = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * r + j;
+          p[e] = exp2_fast(__builtin_fmaf(sacc[e], c_log2, -l4[j]));
+          ds[e] = p[e] * (pacc[e] - d4[j]);
         }
       }
+      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        // element 4 r + j: query qb*32 + 8 r + 4 hh + j
-        float p[16], ds[16];
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 pu, du;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 l4 = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
-          const f32x4 d4 = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int e = 4 * r + j;
-            p[e] = exp2_fast(__builtin_fmaf(sacc[qb][e], c_log2, -l4[j]));
-            ds[e] = kDK ? p[e] * (pacc[qb][e] - d4[j]) : 0.0f;
-          }
+        for (int w = 0; w < 4; ++w) {
+          pu[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
+          du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
         }
-        // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
+        const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          u32x4 pu, du;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            pu[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
-            du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
-          }
-          const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
-#pragma unroll
-          for (int db = 0; db < G::kDB; ++db) {
-            if (kDV)
-              dvacc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), dvacc[db]);
-            if (kDK)
-              dkacc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dkacc[db]);
-          }
-        }
-      }
-    } else {
-      // d = 64 (two waves per SIMD): block by block, the other wave fills in
-#pragma unroll
-      for (int qb = 0; qb < kTRows / 32; ++qb) {
-        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < G::kKSteps; ++s) {
-          const bf16x8 qa = lds_row(qtile + qb * 32 * D * 2, off.row[s]);
-          const bf16x8 da = lds_row(dotile + qb * 32 * D * 2, off.row[s]);
-          sacc = mfma32x32x16(qa, kf[s], sacc);
-          pacc = mfma32x32x16(da, vf[s], pacc);
-        }
-        // element 4 r + j: query qb*32 + 8 r + 4 hh + j
-        float p[16], ds[16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 l4 = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
-          const f32x4 d4 = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int e = 4 * r + j;
-            p[e] = exp2_fast(__builtin_fmaf(sacc[e], c_log2, -l4[j]));
-            ds[e] = p[e] * (pacc[e] - d4[j]);
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          u32x4 pu, du;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            pu[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
-            du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
-          }
-          const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
-#pragma unroll
-          for (int db = 0; db < G::kDB; ++db) {
-            dvacc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), dvacc[db]);
-            dkacc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dkacc[db]);
-          }
+        for (int db = 0; db < G::kDB; ++db) {
+          dvacc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), dvacc[db]);
+          dkacc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), dkacc[db]);
         }
       }
     }
@@ -414,8 +361,218 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   }
 
   if (krow < N) {
-    if (kDK) store_rowT<D>(dkacc, dk + (head_kv + krow) * D, scale, hh);
-    if (kDV) store_rowT<D>(dvacc, dv + (head_kv + krow) * D, 1.0f, hh);
+    store_rowT<D>(dkacc, dk + (head_kv + krow) * D, scale, hh);
+    store_rowT<D>(dvacc, dv + (head_kv + krow) * D, 1.0f, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV at head dim 128: one workgroup of eight waves (two per SIMD) per
+// 128 keys of K/V head (b, kvh), two roles per 32 keys.  Waves 0..3 ("P
+// waves") hold K, compute S = Q K^T and P = exp2(S c - lse), hand P (fp32)
+// to their partner wave through LDS and accumulate dV^T += dO^T P; they also
+// issue the loads.  Waves 4..7 ("dS waves") hold V, compute dP = dO V^T,
+// take P from LDS, form dS = P (dP - D) and accumulate dK^T += Q^T dS.  S is
+// computed once per block (four products; one wave holding K, V, dK and dV
+// would need ~370 registers, one wave per SIMD), and each wave's vector work
+// runs beside its partner's products: the dS waves work one query tile
+// behind, so neither waits for the other inside a step.  Three Q / dO
+// stages: the P waves read tile t while the dS waves read tile t - 1 and
+// tile t + 1 loads.
+template <int D>
+__global__ __launch_bounds__(2 * kBThreads, 1)
+void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                             const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                             const float* __restrict__ lse, const float* __restrict__ dvec,
+                             __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Hq, int Hkv,
+                             int N, float c_log2, float scale, int n_ktiles, uint32_t n_xcd) {
+  static_assert(D == 128, "head dim 64 runs attn_bwd_dkdv_kernel");
+  using G = BGeo<D>;
+  constexpr uint32_t kTileB = G::kTile * 2;
+  constexpr uint32_t kStageB = 2 * kTileB + 2 * kTRows * 4;
+  constexpr int kQB = kTRows / 32;
+  constexpr uint32_t kPB = (uint32_t)kWave * kQB * 16 * 4;   // P of one wave-step, fp32
+  constexpr int kNStage = 3;
+  __shared__ __align__(16) unsigned char smem[kNStage * kStageB + kBWaves * kPB];
+  const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool is_p = wave8 < kBWaves;
+  const int wave = wave8 & (kBWaves - 1);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const uint32_t pbuf = lds + kNStage * kStageB + (uint32_t)wave * kPB + (uint32_t)lane * 16;
+
+  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
+  const int kt = (int)(logical % (uint32_t)n_ktiles);
+  const uint32_t rest = logical / (uint32_t)n_ktiles;
+  const int kvh = (int)(rest % (uint32_t)Hkv);
+  const int b = (int)(rest / (uint32_t)Hkv);
+  const int64_t head_kv = ((int64_t)b * Hkv + kvh) * (int64_t)N;
+  const int n_qrows = (Hq / Hkv) * N;
+  const int64_t head_q = ((int64_t)b * Hkv + kvh) * (int64_t)n_qrows;
+
+  const int krow = kt * kWgRows + wave * kWRows + l32;   // this lane's key
+  bf16x8 kvf[G::kKSteps];                                // K (P waves) or V (dS waves)
+  load_rowfrags<D>(kvf, (is_p ? k : v) + head_kv * D, krow, N, hh);
+
+  const TileOffsets<D> off = tile_offsets<D>(lane, wave);
+  f32x16 acc[G::kDB];                                    // dV^T (P waves) or dK^T (dS waves)
+#pragma unroll
+  for (int i = 0; i < G::kDB; ++i) acc[i] = f32x16{};
+
+  const int n_steps = (n_qrows + kTRows - 1) / kTRows;
+  // Loads of step t into stage t % 3 (P waves), as in attn_bwd_dkdv_kernel:
+  // the row statistics first and scaled only when committed, so no wait
+  // for them covers the tile loads.
+  float st_lse = 0.0f, st_d = 0.0f;
+  auto issue = [&](int t) {
+    const int q0 = t * kTRows;
+    const uint32_t stage = lds + (uint32_t)(t % kNStage) * kStageB;
+    if (tid < kTRows) {
+      const int row = q0 + tid;
+      st_lse = row < n_qrows ? lse[head_q + row] : INFINITY;
+      st_d = row < n_qrows ? dvec[head_q + row] : 0.0f;
+    }
+    dma_tile<D>(q + head_q * D, q0, n_qrows, stage, wave, off.dvoff);
+    dma_tile<D>(dout + head_q * D, q0, n_qrows, stage + kTileB, wave, off.dvoff);
+  };
+  auto commit = [&](int t) {
+    if (tid < kTRows) {
+      const uint32_t stage = lds + (uint32_t)(t % kNStage) * kStageB;
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + tid * 4) = st_lse * kLog2e;
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + kTRows * 4 + tid * 4) = st_d;
+    }
+  };
+
+  if (is_p) issue(0);
+  // every wave: its K or V fragments, and (P waves) tile 0, have landed
+  wait_vm();
+  if (is_p) commit(0);
+  __syncthreads();
+
+  // Step t (stage st = t % 3): the P waves run query tile t; the dS waves
+  // run tile t - 1 (stage (t + 2) % 3), whose P their partner wrote in
+  // step t - 1.  Before the middle barrier: S of tile t / the read of
+  // P(t - 1) and dP of tile t - 1; after it: the weights, P(t) into LDS
+  // (one buffer per pair: P(t - 1) has been read) and dV / dS and dK.
+  // Step n_steps only drains the dS waves.
+  auto q_step = [&](const int t, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    if (is_p) {
+      const uint32_t stage = lds + (uint32_t)st * kStageB;
+      const uint32_t qtile = stage, dotile = stage + kTileB;
+      const uint32_t lse_s = stage + 2 * kTileB;
+      const bool run = t < n_steps;
+      if (run && t + 1 < n_steps) issue(t + 1);
+      f32x16 sacc[kQB];
+      if (run) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          sacc[qb] = f32x16{};
+#pragma unroll
+          for (int s = 0; s < G::kKSteps; ++s)
+            sacc[qb] = mfma32x32x16(lds_row(qtile + qb * 32 * D * 2, off.row[s]), kvf[s], sacc[qb]);
+        }
+      }
+      // P is in LDS (LDS order only: a full __syncthreads would also wait
+      // for the next tile's loads still in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (run) {
+        float p[kQB][16];
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // element 4 r + j: query qb*32 + 8 r + 4 hh + j
+            const f32x4 l4 = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+            f32x4 pv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              p[qb][4 * r + j] = exp2_fast(__builtin_fmaf(sacc[qb][4 * r + j], c_log2, -l4[j]));
+              pv[j] = p[qb][4 * r + j];
+            }
+            *(lds_f32x4*)(uintptr_t)(pbuf + (uint32_t)(qb * 4 + r) * kWave * 16) = pv;
+          }
+        // dV^T += dO^T P over the two 16-query k-steps of each block
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            u32x4 pu;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) pu[w] = pack_bf16x2(p[qb][8 * s2 + 2 * w], p[qb][8 * s2 + 2 * w + 1]);
+            const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
+#pragma unroll
+            for (int db = 0; db < G::kDB; ++db)
+              acc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), acc[db]);
+          }
+      }
+      // unconditional: the compiler then knows no load is in flight at the
+      // next step's start (else it waits for the next tile's loads there)
+      wait_vm();
+      if (run && t + 1 < n_steps) commit(t + 1);
+    } else {
+      const uint32_t stage = lds + (uint32_t)((st + kNStage - 1) % kNStage) * kStageB;
+      const uint32_t qtile = stage, dotile = stage + kTileB;
+      const uint32_t d_s = stage + 2 * kTileB + kTRows * 4;
+      const bool run = t > 0;
+      f32x16 pacc[kQB];
+      f32x4 pv[kQB][4];
+      if (run) {
+        // P of tile t - 1, written by the partner last step; dP = dO V^T
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            pv[qb][r] = *(const lds_f32x4*)(uintptr_t)(pbuf + (uint32_t)(qb * 4 + r) * kWave * 16);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          pacc[qb] = f32x16{};
+#pragma unroll
+          for (int s = 0; s < G::kKSteps; ++s)
+            pacc[qb] = mfma32x32x16(lds_row(dotile + qb * 32 * D * 2, off.row[s]), kvf[s], pacc[qb]);
+        }
+      }
+      // P is in LDS (LDS order only: a full __syncthreads would also wait
+      // for the next tile's loads still in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (run) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          float ds[16];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const f32x4 d4 = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ds[4 * r + j] = pv[qb][r][j] * (pacc[qb][4 * r + j] - d4[j]);
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            u32x4 du;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
+            const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
+#pragma unroll
+            for (int db = 0; db < G::kDB; ++db)
+              acc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), acc[db]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  };
+  for (int t = 0; t <= n_steps; t += kNStage) {
+    q_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 <= n_steps) q_step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 <= n_steps) q_step(t + 2, std::integral_constant<int, 2>{});
+  }
+
+  if (krow < N) {
+    if (is_p) store_rowT<D>(acc, dv + (head_kv + krow) * D, 1.0f, hh);
+    else store_rowT<D>(acc, dk + (head_kv + krow) * D, scale, hh);
   }
 }
 
@@ -541,19 +698,22 @@ hipError_t launch_d(const FwdArgs& a, const BwdArgs& g) {
   if (e != hipSuccess) return e;
   const int n_kt = (a.N + kWgRows - 1) / kWgRows;
   const uint64_t grid1 = (uint64_t)n_kt * a.Hkv * a.B;
-  // head dim 128: dV and dK in two passes (see the kernel); 64: one pass
-  constexpr int kPasses = D == 128 ? 2 : 1;
-  for (int pass = 0; pass < kPasses; ++pass) {
-    auto kern = D == 128 ? (pass == 0 ? attn_bwd_dkdv_kernel<D, 1> : attn_bwd_dkdv_kernel<D, 2>)
-                         : attn_bwd_dkdv_kernel<D, 0>;
-    hipLaunchKernelGGL(kern, dim3((uint32_t)grid1), dim3(kBThreads), 0, a.stream,
-                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+  // head dim 128: two waves per 32 keys (attn_bwd_dkdv_rs_kernel); 64: one
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_rs_kernel<D>), dim3((uint32_t)grid1), dim3(2 * kBThreads), 0,
+                       a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                        static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(g.dout), a.lse,
                        g.dvec, static_cast<__bf16*>(g.dk), static_cast<__bf16*>(g.dv), a.Hq, a.Hkv,
                        a.N, c_log2, a.scale, n_kt, (uint32_t)a.n_xcd);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((uint32_t)grid1), dim3(kBThreads), 0,
+                       a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(g.dout), a.lse,
+                       g.dvec, static_cast<__bf16*>(g.dk), static_cast<__bf16*>(g.dv), a.Hq, a.Hkv,
+                       a.N, c_log2, a.scale, n_kt, (uint32_t)a.n_xcd);
   }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int n_qt = (int)(((uint64_t)(a.Hq / a.Hkv) * a.N + kWgRows - 1) / kWgRows);
   const uint64_t grid2 = (uint64_t)n_qt * a.Hkv * a.B;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((uint32_t)grid2), dim3(kBThreads), 0, a.stream,
