@@ -459,115 +459,137 @@ void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restr
   // P(t - 1) and dP of tile t - 1; after it: the weights, P(t) into LDS
   // (one buffer per pair: P(t - 1) has been read) and dV / dS and dK.
   // Step n_steps only drains the dS waves.
-  auto q_step = [&](const int t, auto stage_c) {
+  // The two roles run separate loops (the same steps and barriers), so no
+  // value is merged between them inside a loop.
+  auto p_step = [&](const int t, auto stage_c) {
     constexpr int st = decltype(stage_c)::value;
-    if (is_p) {
-      const uint32_t stage = lds + (uint32_t)st * kStageB;
-      const uint32_t qtile = stage, dotile = stage + kTileB;
-      const uint32_t lse_s = stage + 2 * kTileB;
-      const bool run = t < n_steps;
-      if (run && t + 1 < n_steps) issue(t + 1);
-      f32x16 sacc[kQB];
-      if (run) {
+    const uint32_t stage = lds + (uint32_t)st * kStageB;
+    const uint32_t qtile = stage, dotile = stage + kTileB;
+    const uint32_t lse_s = stage + 2 * kTileB;
+    const bool run = t < n_steps;
+    if (run && t + 1 < n_steps) issue(t + 1);
+    f32x16 sacc[kQB];
+    f32x4 l4v[kQB][4];
+    if (run) {
+      // lse of the tile's rows (committed last step), read beside the products
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          sacc[qb] = f32x16{};
+      for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-          for (int s = 0; s < G::kKSteps; ++s)
-            sacc[qb] = mfma32x32x16(lds_row(qtile + qb * 32 * D * 2, off.row[s]), kvf[s], sacc[qb]);
+        for (int r = 0; r < 4; ++r)
+          l4v[qb][r] = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        sacc[qb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < G::kKSteps; ++s)
+          sacc[qb] = mfma32x32x16(lds_row(qtile + qb * 32 * D * 2, off.row[s]), kvf[s], sacc[qb]);
+      }
+    }
+    // past this barrier the partner has read P(t - 1), so P(t) may take its
+    // place (LDS order only: a full __syncthreads would also wait for the
+    // next tile's loads still in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (run) {
+      float p[kQB][16];
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // element 4 r + j: query qb*32 + 8 r + 4 hh + j
+          const f32x4 l4 = l4v[qb][r];
+          f32x4 pv;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[qb][4 * r + j] = exp2_fast(__builtin_fmaf(sacc[qb][4 * r + j], c_log2, -l4[j]));
+            pv[j] = p[qb][4 * r + j];
+          }
+          *(lds_f32x4*)(uintptr_t)(pbuf + (uint32_t)(qb * 4 + r) * kWave * 16) = pv;
         }
-      }
-      // P is in LDS (LDS order only: a full __syncthreads would also wait
-      // for the next tile's loads still in flight)
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (run) {
-        float p[kQB][16];
+      // dV^T += dO^T P over the two 16-query k-steps of each block
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
+      for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // element 4 r + j: query qb*32 + 8 r + 4 hh + j
-            const f32x4 l4 = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
-            f32x4 pv;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 pu;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              p[qb][4 * r + j] = exp2_fast(__builtin_fmaf(sacc[qb][4 * r + j], c_log2, -l4[j]));
-              pv[j] = p[qb][4 * r + j];
-            }
-            *(lds_f32x4*)(uintptr_t)(pbuf + (uint32_t)(qb * 4 + r) * kWave * 16) = pv;
-          }
-        // dV^T += dO^T P over the two 16-query k-steps of each block
+          for (int w = 0; w < 4; ++w) pu[w] = pack_bf16x2(p[qb][8 * s2 + 2 * w], p[qb][8 * s2 + 2 * w + 1]);
+          const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            u32x4 pu;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) pu[w] = pack_bf16x2(p[qb][8 * s2 + 2 * w], p[qb][8 * s2 + 2 * w + 1]);
-            const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
-#pragma unroll
-            for (int db = 0; db < G::kDB; ++db)
-              acc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), acc[db]);
-          }
-      }
-      // unconditional: the compiler then knows no load is in flight at the
-      // next step's start (else it waits for the next tile's loads there)
-      wait_vm();
-      if (run && t + 1 < n_steps) commit(t + 1);
-    } else {
-      const uint32_t stage = lds + (uint32_t)((st + kNStage - 1) % kNStage) * kStageB;
-      const uint32_t qtile = stage, dotile = stage + kTileB;
-      const uint32_t d_s = stage + 2 * kTileB + kTRows * 4;
-      const bool run = t > 0;
-      f32x16 pacc[kQB];
-      f32x4 pv[kQB][4];
-      if (run) {
-        // P of tile t - 1, written by the partner last step; dP = dO V^T
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            pv[qb][r] = *(const lds_f32x4*)(uintptr_t)(pbuf + (uint32_t)(qb * 4 + r) * kWave * 16);
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          pacc[qb] = f32x16{};
-#pragma unroll
-          for (int s = 0; s < G::kKSteps; ++s)
-            pacc[qb] = mfma32x32x16(lds_row(dotile + qb * 32 * D * 2, off.row[s]), kvf[s], pacc[qb]);
+          for (int db = 0; db < G::kDB; ++db)
+            acc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), acc[db]);
         }
+    }
+    // unconditional: the compiler then knows no load is in flight at the
+    // next step's start (else it waits for the next tile's loads there)
+    wait_vm();
+    if (run && t + 1 < n_steps) commit(t + 1);
+    __syncthreads();
+  };
+  auto ds_step = [&](const int t, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    const uint32_t stage = lds + (uint32_t)((st + kNStage - 1) % kNStage) * kStageB;
+    const uint32_t qtile = stage, dotile = stage + kTileB;
+    const uint32_t d_s = stage + 2 * kTileB + kTRows * 4;
+    const bool run = t > 0;
+    f32x16 pacc[kQB];
+    f32x4 pv[kQB][4], d4v[kQB][4];
+    if (run) {
+      // P of tile t - 1, written by the partner last step, and D of its
+      // rows; dP = dO V^T
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[qb][r] = *(const lds_f32x4*)(uintptr_t)(pbuf + (uint32_t)(qb * 4 + r) * kWave * 16);
+          d4v[qb][r] = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+        }
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        pacc[qb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < G::kKSteps; ++s)
+          pacc[qb] = mfma32x32x16(lds_row(dotile + qb * 32 * D * 2, off.row[s]), kvf[s], pacc[qb]);
       }
-      // P is in LDS (LDS order only: a full __syncthreads would also wait
-      // for the next tile's loads still in flight)
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (run) {
+    }
+    // P(t - 1) has been read before the partner overwrites it (LDS order
+    // only, as in p_step)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (run) {
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          float ds[16];
+      for (int qb = 0; qb < kQB; ++qb) {
+        float ds[16];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const f32x4 d4 = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 d4 = d4v[qb][r];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ds[4 * r + j] = pv[qb][r][j] * (pacc[qb][4 * r + j] - d4[j]);
-          }
+          for (int j = 0; j < 4; ++j) ds[4 * r + j] = pv[qb][r][j] * (pacc[qb][4 * r + j] - d4[j]);
+        }
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            u32x4 du;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 du;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
-            const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
+          for (int w = 0; w < 4; ++w) du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
+          const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
 #pragma unroll
-            for (int db = 0; db < G::kDB; ++db)
-              acc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), acc[db]);
-          }
+          for (int db = 0; db < G::kDB; ++db)
+            acc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), acc[db]);
         }
       }
     }
     __syncthreads();
   };
-  for (int t = 0; t <= n_steps; t += kNStage) {
-    q_step(t, std::integral_constant<int, 0>{});
-    if (t + 1 <= n_steps) q_step(t + 1, std::integral_constant<int, 1>{});
-    if (t + 2 <= n_steps) q_step(t + 2, std::integral_constant<int, 2>{});
+  if (is_p) {
+    for (int t = 0; t <= n_steps; t += kNStage) {
+      p_step(t, std::integral_constant<int, 0>{});
+      if (t + 1 <= n_steps) p_step(t + 1, std::integral_constant<int, 1>{});
+      if (t + 2 <= n_steps) p_step(t + 2, std::integral_constant<int, 2>{});
+    }
+  } else {
+    for (int t = 0; t <= n_steps; t += kNStage) {
+      ds_step(t, std::integral_constant<int, 0>{});
+      if (t + 1 <= n_steps) ds_step(t + 1, std::integral_constant<int, 1>{});
+      if (t + 2 <= n_steps) ds_step(t + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   if (krow < N) {
