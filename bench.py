@@ -47,7 +47,7 @@ KERNEL_SOURCES = {
 def kernel_source_hash(workload: str) -> str:
     """Hash of the sources of the kernel that runs `workload` (a counter
     summary taken on other sources no longer describes that kernel)."""
-    w = workloads.WORKLOADS[workload]
+    w = workloads.ALL[workload]
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[(w.dtype, w.d)] + _COMMON_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -328,7 +328,7 @@ def main():
     # so the default warm-up is long enough for that at every workload
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default=workloads.DEFAULT_BENCH, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--workload", default=workloads.DEFAULT_BENCH, choices=sorted(workloads.ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -372,7 +372,7 @@ def main():
 
     from exact_io_aware_73_amd import attn
 
-    w = workloads.WORKLOADS[args.workload]
+    w = workloads.ALL[args.workload]
     torch.cuda.set_device(0)
     q, k, v = workloads.make_inputs(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
@@ -452,8 +452,9 @@ def main():
     sp_bytes = w.B * w.Hq * w.N * w.N * (4 + w.elem_bytes)
     if not w.materialized and not args.no_materialized and not fp8:
         materialized = {"skipped": f"S and P would take {sp_bytes / 1e9:.1f} GB; this workload "
-                                   "runs only the tiled path (long_b4_h32_n4096_d128 and "
-                                   "gpt2_medium_b64_h16_n1024_d64 carry the comparison)"}
+                                   "runs only the tiled path (long_b4_h32_n4096_d128, "
+                                   "gpt2_medium_b64_h16_n1024_d64 and the sequence-length "
+                                   "sweep up to N = 8192 carry the comparison)"}
     elif not args.no_materialized and not fp8 and sp_bytes < (64 << 30):
         s = torch.empty((w.B, w.Hq, w.N, w.N), dtype=torch.float32, device="cuda")
         p = torch.empty((w.B, w.Hq, w.N, w.N), dtype=w.torch_dtype, device="cuda")

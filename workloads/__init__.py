@@ -80,6 +80,25 @@ WORKLOADS = {
 # the long sequence lengths where the pages place the method's gain.
 DEFAULT_BENCH = "long_context_b1_h8_n32768_d128"
 
+# The sequence-length sweep ("3.1 性能模型：用 Roofline 与算术强度算清为什么快",
+# section 3.1.5: every variable fixed but the sequence length, both arms
+# measured at each length): the long_b4 configuration (B = 4, 32 heads,
+# d = 128, bf16) at N = 512 ... 16384.  The comparison arm runs where its S
+# and P fit (N <= 8192: 51.5 GB); at N = 16384 they would take 206 GB.
+SWEEP_N = (512, 1024, 2048, 4096, 8192, 16384)
+SWEEP = {
+    w.name: w
+    for w in [
+        Workload(f"sweep_b4_h32_n{n}_d128", 4, 32, 32, n, 128, "bf16", 8000 + n,
+                 description=f"sequence-length sweep at B = 4, 32 heads, d = 128: N = {n}",
+                 materialized=n <= 8192)
+        for n in SWEEP_N
+    ]
+}
+
+# Every name bench.py accepts.
+ALL = {**WORKLOADS, **SWEEP}
+
 
 def _randn(shape, seed: int) -> torch.Tensor:
     g = torch.Generator(device="cpu")
