@@ -52,3 +52,17 @@ def test_default_workload_is_the_largest_single_gpu_configuration():
               key=lambda w: 4 * w.B * w.Hq * w.N * w.N * w.d)
     assert workloads.DEFAULT_BENCH == big.name == "long_context_b1_h8_n32768_d128"
     assert not workloads.WORKLOADS[workloads.DEFAULT_BENCH].materialized
+
+
+def test_sequence_length_sweep_fixes_everything_but_n():
+    """The sweep of the measurement section: one configuration at every
+    length, the comparison path wherever its S and P fit the bench's 64 GiB
+    cap, and none of it among the configurations the default is chosen from."""
+    sw = list(workloads.SWEEP.values())
+    assert [w.N for w in sw] == sorted(w.N for w in sw) and len(sw) >= 5
+    assert {(w.B, w.Hq, w.Hkv, w.d, w.dtype) for w in sw} == {(4, 32, 32, 128, "bf16")}
+    for w in sw:
+        sp = w.B * w.Hq * w.N * w.N * (4 + w.elem_bytes)
+        assert w.materialized == (sp < (64 << 30)), w.name
+        assert w.name in workloads.ALL and w.name not in workloads.WORKLOADS
+    assert set(workloads.WORKLOADS) <= set(workloads.ALL)
