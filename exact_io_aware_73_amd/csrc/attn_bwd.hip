@@ -366,19 +366,54 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   }
 }
 
+// acc[qb] = rows qb*32 .. +31 of the LDS tile times the wave's fragments
+// (32 x 32 keys, over d), the row reads issued eight ahead of their products
+// in a fixed order (the compiler otherwise waits on each read right before
+// its product); extra(i), i < 8, is run after the i-th product of the second
+// block (further LDS reads that go with the step).
+template <int D, typename Extra>
+__device__ __forceinline__ void row_products(f32x16 (&acc)[2], uint32_t tile, const TileOffsets<D>& off,
+                                             const bf16x8 (&frag)[BGeo<D>::kKSteps], Extra extra) {
+  constexpr int kS = BGeo<D>::kKSteps;
+  static_assert(kS == 8, "eight k-steps per block");
+  bf16x8 a0[kS], a1[kS];
+#pragma unroll
+  for (int s = 0; s < kS; ++s) a0[s] = lds_row(tile, off.row[s]);
+  __builtin_amdgcn_sched_barrier(0);
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < kS; ++s) {
+    acc[0] = mfma32x32x16(a0[s], frag[s], acc[0]);
+    a1[s] = lds_row(tile + 32 * D * 2, off.row[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int s = 0; s < kS; ++s) {
+    acc[1] = mfma32x32x16(a1[s], frag[s], acc[1]);
+    extra(s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK and dV at head dim 128: one workgroup of eight waves (two per SIMD) per
 // 128 keys of K/V head (b, kvh), two roles per 32 keys.  Waves 0..3 ("P
 // waves") hold K, compute S = Q K^T and P = exp2(S c - lse), hand P (fp32)
 // to their partner wave through LDS and accumulate dV^T += dO^T P; they also
-// issue the loads.  Waves 4..7 ("dS waves") hold V, compute dP = dO V^T,
-// take P from LDS, form dS = P (dP - D) and accumulate dK^T += Q^T dS.  S is
-// computed once per block (four products; one wave holding K, V, dK and dV
-// would need ~370 registers, one wave per SIMD), and each wave's vector work
-// runs beside its partner's products: the dS waves work one query tile
-// behind, so neither waits for the other inside a step.  Three Q / dO
-// stages: the P waves read tile t while the dS waves read tile t - 1 and
-// tile t + 1 loads.
+// issue the loads.  Waves 4..7 ("dS waves") hold V, take P from LDS, form
+// dS = P (dP - D), accumulate dK^T += Q^T dS and compute dP = dO V^T for
+// the next step.  S is computed once per block (four products; one wave
+// holding K, V, dK and dV would need ~370 registers, one wave per SIMD).
+//
+// In step t the P wave runs query tile t (products, weights, products) and
+// the dS wave finishes tile t - 1 (weights first, then dK) and then forms
+// dP of tile t, so each wave's vector work runs while its partner on the
+// same SIMD issues products.  P goes through two LDS buffers per pair (tile
+// t into buffer t % 2), so one barrier per step orders the hand-over: P(t)
+// is read in step t + 1 and its buffer written again in step t + 2.  LDS
+// slots: Q of tiles t - 1, t and t + 1 (three), dO of tiles t and t + 1
+// (two), lse and D beside each Q slot.
 template <int D>
 __global__ __launch_bounds__(2 * kBThreads, 1)
 void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -389,11 +424,16 @@ void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restr
   static_assert(D == 128, "head dim 64 runs attn_bwd_dkdv_kernel");
   using G = BGeo<D>;
   constexpr uint32_t kTileB = G::kTile * 2;
-  constexpr uint32_t kStageB = 2 * kTileB + 2 * kTRows * 4;
+  constexpr uint32_t kStatB = 2 * kTRows * 4;                // lse and D of one tile
   constexpr int kQB = kTRows / 32;
   constexpr uint32_t kPB = (uint32_t)kWave * kQB * 16 * 4;   // P of one wave-step, fp32
-  constexpr int kNStage = 3;
-  __shared__ __align__(16) unsigned char smem[kNStage * kStageB + kBWaves * kPB];
+  constexpr int kNQ = 3, kNO = 2, kNP = 2;                   // Q, dO and P buffers
+  constexpr uint32_t kQOff = 0;
+  constexpr uint32_t kOOff = kQOff + kNQ * kTileB;
+  constexpr uint32_t kSOff = kOOff + kNO * kTileB;
+  constexpr uint32_t kPOff = kSOff + kNQ * kStatB;
+  constexpr uint32_t kPSlot = kBWaves * kPB;
+  __shared__ __align__(16) unsigned char smem[kPOff + kNP * kPSlot];
   const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
 
   const int tid = threadIdx.x;
@@ -403,7 +443,7 @@ void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restr
   const int wave = wave8 & (kBWaves - 1);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const uint32_t pbuf = lds + kNStage * kStageB + (uint32_t)wave * kPB + (uint32_t)lane * 16;
+  const uint32_t pbuf = lds + kPOff + (uint32_t)wave * kPB + (uint32_t)lane * 16;
 
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
   const int kt = (int)(logical % (uint32_t)n_ktiles);
@@ -424,75 +464,54 @@ void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restr
   for (int i = 0; i < G::kDB; ++i) acc[i] = f32x16{};
 
   const int n_steps = (n_qrows + kTRows - 1) / kTRows;
-  // Loads of step t into stage t % 3 (P waves), as in attn_bwd_dkdv_kernel:
-  // the row statistics first and scaled only when committed, so no wait
-  // for them covers the tile loads.
+  // Loads of tile t (P waves): the row statistics first and scaled only
+  // when committed, so no wait for them covers the tile loads.
   float st_lse = 0.0f, st_d = 0.0f;
-  auto issue = [&](int t) {
+  auto issue = [&](int t, uint32_t qslot, uint32_t oslot) {
     const int q0 = t * kTRows;
-    const uint32_t stage = lds + (uint32_t)(t % kNStage) * kStageB;
     if (tid < kTRows) {
       const int row = q0 + tid;
       st_lse = row < n_qrows ? lse[head_q + row] : INFINITY;
       st_d = row < n_qrows ? dvec[head_q + row] : 0.0f;
     }
-    dma_tile<D>(q + head_q * D, q0, n_qrows, stage, wave, off.dvoff);
-    dma_tile<D>(dout + head_q * D, q0, n_qrows, stage + kTileB, wave, off.dvoff);
+    dma_tile<D>(q + head_q * D, q0, n_qrows, qslot, wave, off.dvoff);
+    dma_tile<D>(dout + head_q * D, q0, n_qrows, oslot, wave, off.dvoff);
   };
-  auto commit = [&](int t) {
+  auto commit = [&](uint32_t sslot) {
     if (tid < kTRows) {
-      const uint32_t stage = lds + (uint32_t)(t % kNStage) * kStageB;
-      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + tid * 4) = st_lse * kLog2e;
-      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + kTRows * 4 + tid * 4) = st_d;
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(sslot + tid * 4) = st_lse * kLog2e;
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(sslot + kTRows * 4 + tid * 4) = st_d;
     }
   };
 
-  if (is_p) issue(0);
+  if (is_p) issue(0, lds + kQOff, lds + kOOff);
   // every wave: its K or V fragments, and (P waves) tile 0, have landed
   wait_vm();
-  if (is_p) commit(0);
+  if (is_p) commit(lds + kSOff);
   __syncthreads();
 
-  // Step t (stage st = t % 3): the P waves run query tile t; the dS waves
-  // run tile t - 1 (stage (t + 2) % 3), whose P their partner wrote in
-  // step t - 1.  Before the middle barrier: S of tile t / the read of
-  // P(t - 1) and dP of tile t - 1; after it: the weights, P(t) into LDS
-  // (one buffer per pair: P(t - 1) has been read) and dV / dS and dK.
-  // Step n_steps only drains the dS waves.
-  // The two roles run separate loops (the same steps and barriers), so no
-  // value is merged between them inside a loop.
-  auto p_step = [&](const int t, auto stage_c) {
-    constexpr int st = decltype(stage_c)::value;
-    const uint32_t stage = lds + (uint32_t)st * kStageB;
-    const uint32_t qtile = stage, dotile = stage + kTileB;
-    const uint32_t lse_s = stage + 2 * kTileB;
-    const bool run = t < n_steps;
-    if (run && t + 1 < n_steps) issue(t + 1);
-    f32x16 sacc[kQB];
-    f32x4 l4v[kQB][4];
-    if (run) {
-      // lse of the tile's rows (committed last step), read beside the products
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          l4v[qb][r] = *(const lds_f32x4*)(uintptr_t)(lse_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+  // Slots of step t are compile-time constants: the loops below run six
+  // steps per trip (the buffer counts 3 and 2 divide 6), c = t % 6.
+  auto p_step = [&](const int t, auto c_) {
+    constexpr int c = decltype(c_)::value;
+    constexpr uint32_t qs = kQOff + (uint32_t)(c % kNQ) * kTileB;
+    constexpr uint32_t os = kOOff + (uint32_t)(c % kNO) * kTileB;
+    constexpr uint32_t ss = kSOff + (uint32_t)(c % kNQ) * kStatB;
+    constexpr uint32_t ps = (uint32_t)(c % kNP) * kPSlot;
+    const bool more = t + 1 < n_steps;
+    if (more)
+      issue(t + 1, lds + kQOff + (uint32_t)((c + 1) % kNQ) * kTileB,
+            lds + kOOff + (uint32_t)((c + 1) % kNO) * kTileB);
+    if (t < n_steps) {
+      const uint32_t qtile = lds + qs, dotile = lds + os;
+      f32x4 l4v[kQB][4];
+      f32x16 sacc[kQB];
+      row_products<D>(sacc, qtile, off, kvf, [&](int i) {
+        l4v[i / 4][i % 4] = *(const lds_f32x4*)(uintptr_t)(lds + ss + ((i / 4) * 32 + 8 * (i % 4) + 4 * hh) * 4);
+      });
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
-        sacc[qb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < G::kKSteps; ++s)
-          sacc[qb] = mfma32x32x16(lds_row(qtile + qb * 32 * D * 2, off.row[s]), kvf[s], sacc[qb]);
-      }
-    }
-    // past this barrier the partner has read P(t - 1), so P(t) may take its
-    // place (LDS order only: a full __syncthreads would also wait for the
-    // next tile's loads still in flight)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (run) {
-      float p[kQB][16];
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
+        float p[16];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           // element 4 r + j: query qb*32 + 8 r + 4 hh + j
@@ -500,70 +519,55 @@ void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restr
           f32x4 pv;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            p[qb][4 * r + j] = exp2_fast(__builtin_fmaf(sacc[qb][4 * r + j], c_log2, -l4[j]));
-            pv[j] = p[qb][4 * r + j];
+            p[4 * r + j] = exp2_fast(__builtin_fmaf(sacc[qb][4 * r + j], c_log2, -l4[j]));
+            pv[j] = p[4 * r + j];
           }
-          *(lds_f32x4*)(uintptr_t)(pbuf + (uint32_t)(qb * 4 + r) * kWave * 16) = pv;
+          *(lds_f32x4*)(uintptr_t)(pbuf + ps + (uint32_t)(qb * 4 + r) * kWave * 16) = pv;
         }
-      // dV^T += dO^T P over the two 16-query k-steps of each block
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
+        // dV^T += dO^T P over the two 16-query k-steps of the block
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           u32x4 pu;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) pu[w] = pack_bf16x2(p[qb][8 * s2 + 2 * w], p[qb][8 * s2 + 2 * w + 1]);
+          for (int w = 0; w < 4; ++w) pu[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
           const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
 #pragma unroll
           for (int db = 0; db < G::kDB; ++db)
             acc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), acc[db]);
         }
+      }
     }
     // unconditional: the compiler then knows no load is in flight at the
     // next step's start (else it waits for the next tile's loads there)
     wait_vm();
-    if (run && t + 1 < n_steps) commit(t + 1);
+    if (more) commit(lds + kSOff + (uint32_t)((c + 1) % kNQ) * kStatB);
     __syncthreads();
   };
-  auto ds_step = [&](const int t, auto stage_c) {
-    constexpr int st = decltype(stage_c)::value;
-    const uint32_t stage = lds + (uint32_t)((st + kNStage - 1) % kNStage) * kStageB;
-    const uint32_t qtile = stage, dotile = stage + kTileB;
-    const uint32_t d_s = stage + 2 * kTileB + kTRows * 4;
-    const bool run = t > 0;
-    f32x16 pacc[kQB];
-    f32x4 pv[kQB][4], d4v[kQB][4];
-    if (run) {
-      // P of tile t - 1, written by the partner last step, and D of its
-      // rows; dP = dO V^T
+  f32x16 pacc[kQB];                                      // dP of the dS wave's next tile
+  auto ds_step = [&](const int t, auto c_) {
+    constexpr int c = decltype(c_)::value;
+    constexpr int cp = (c + 5) % 6;                      // (t - 1) % 6
+    constexpr uint32_t qs = kQOff + (uint32_t)(cp % kNQ) * kTileB;
+    constexpr uint32_t ds_off = kSOff + (uint32_t)(cp % kNQ) * kStatB + kTRows * 4;
+    constexpr uint32_t ps = (uint32_t)(cp % kNP) * kPSlot;
+    constexpr uint32_t os = kOOff + (uint32_t)(c % kNO) * kTileB;
+    if (t > 0) {
+      // tile t - 1: P written by the partner last step, D of its rows, dP
+      // from last step
+      const uint32_t qtile = lds + qs;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
+      for (int qb = 0; qb < kQB; ++qb) {
+        f32x4 pv[4], d4v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pv[qb][r] = *(const lds_f32x4*)(uintptr_t)(pbuf + (uint32_t)(qb * 4 + r) * kWave * 16);
-          d4v[qb][r] = *(const lds_f32x4*)(uintptr_t)(d_s + (qb * 32 + 8 * r + 4 * hh) * 4);
+          pv[r] = *(const lds_f32x4*)(uintptr_t)(pbuf + ps + (uint32_t)(qb * 4 + r) * kWave * 16);
+          d4v[r] = *(const lds_f32x4*)(uintptr_t)(lds + ds_off + (qb * 32 + 8 * r + 4 * hh) * 4);
         }
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        pacc[qb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < G::kKSteps; ++s)
-          pacc[qb] = mfma32x32x16(lds_row(dotile + qb * 32 * D * 2, off.row[s]), kvf[s], pacc[qb]);
-      }
-    }
-    // P(t - 1) has been read before the partner overwrites it (LDS order
-    // only, as in p_step)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (run) {
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
         float ds[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 d4 = d4v[qb][r];
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) ds[4 * r + j] = pv[qb][r][j] * (pacc[qb][4 * r + j] - d4[j]);
-        }
+          for (int j = 0; j < 4; ++j) ds[4 * r + j] = pv[r][j] * (pacc[qb][4 * r + j] - d4v[r][j]);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           u32x4 du;
@@ -576,19 +580,29 @@ void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restr
         }
       }
     }
+    if (t < n_steps) {
+      // dP = dO V^T of tile t, used next step
+      row_products<D>(pacc, lds + os, off, kvf, [](int) {});
+    }
     __syncthreads();
   };
   if (is_p) {
-    for (int t = 0; t <= n_steps; t += kNStage) {
+    for (int t = 0; t <= n_steps; t += 6) {
       p_step(t, std::integral_constant<int, 0>{});
       if (t + 1 <= n_steps) p_step(t + 1, std::integral_constant<int, 1>{});
       if (t + 2 <= n_steps) p_step(t + 2, std::integral_constant<int, 2>{});
+      if (t + 3 <= n_steps) p_step(t + 3, std::integral_constant<int, 3>{});
+      if (t + 4 <= n_steps) p_step(t + 4, std::integral_constant<int, 4>{});
+      if (t + 5 <= n_steps) p_step(t + 5, std::integral_constant<int, 5>{});
     }
   } else {
-    for (int t = 0; t <= n_steps; t += kNStage) {
+    for (int t = 0; t <= n_steps; t += 6) {
       ds_step(t, std::integral_constant<int, 0>{});
       if (t + 1 <= n_steps) ds_step(t + 1, std::integral_constant<int, 1>{});
       if (t + 2 <= n_steps) ds_step(t + 2, std::integral_constant<int, 2>{});
+      if (t + 3 <= n_steps) ds_step(t + 3, std::integral_constant<int, 3>{});
+      if (t + 4 <= n_steps) ds_step(t + 4, std::integral_constant<int, 4>{});
+      if (t + 5 <= n_steps) ds_step(t + 5, std::integral_constant<int, 5>{});
     }
   }
 
