@@ -31,7 +31,22 @@ from exact_io_aware_73_amd import accounting as acc  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak; HBM bytes vs Q/K/V/O min"
 # the sources each workload's fused kernel is built from, by I/O dtype and head dim
-_COMMON_SOURCES = ["exact_io_aware_73_amd/csrc/device_common.hpp", "exact_io_aware_73_amd/build.py"]
+_COMMON_SOURCES = ["exact_io_aware_73_amd/csrc/device_common.hpp"]
+
+
+def _hash_sources(rels) -> str:
+    """Hash of the given sources, the shared header and the compile flags
+    that apply to them (the global flags and each file's own), so an edit to
+    another file's flags leaves the hash alone."""
+    from exact_io_aware_73_amd import build as B
+    h = hashlib.sha256()
+    for rel in list(rels) + _COMMON_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    flags = [" ".join(B.CFLAGS)] + [f"{os.path.basename(r)}: {' '.join(B.FILE_FLAGS.get(os.path.basename(r), []))}"
+                                    for r in rels]
+    h.update("\n".join(flags).encode())
+    return h.hexdigest()[:16]
 KERNEL_SOURCES = {
     ("bf16", 64): ["exact_io_aware_73_amd/csrc/attn_fwd_bf16_rows32.hip"],
     # head dim 128 runs rows64 or rows32 by shape (the rule is in kernels.hpp)
@@ -48,11 +63,7 @@ def kernel_source_hash(workload: str) -> str:
     """Hash of the sources of the kernel that runs `workload` (a counter
     summary taken on other sources no longer describes that kernel)."""
     w = workloads.ALL[workload]
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[(w.dtype, w.d)] + _COMMON_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return _hash_sources(KERNEL_SOURCES[(w.dtype, w.d)])
 
 
 # the sources of the three kernels of the materialising path
@@ -61,11 +72,7 @@ MATERIALIZED_SOURCES = ["exact_io_aware_73_amd/csrc/attn_materialized.hip",
 
 
 def materialized_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in MATERIALIZED_SOURCES + _COMMON_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return _hash_sources(MATERIALIZED_SOURCES)
 
 
 def _counters(path: str, sha: str):
@@ -102,11 +109,7 @@ BACKWARD_SOURCES = ["exact_io_aware_73_amd/csrc/attn_bwd.hip", "exact_io_aware_7
 
 
 def backward_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in BACKWARD_SOURCES + _COMMON_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return _hash_sources(BACKWARD_SOURCES)
 
 
 def backward_traffic_from_profiles(workload: str, profiles_dir: str | None = None):

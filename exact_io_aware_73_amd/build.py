@@ -37,6 +37,10 @@ CFLAGS = [
 FILE_FLAGS = {
     "attn_fwd_bf16_rows64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "attn_fwd_bf16_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the d = 128 dK/dV kernel: S and dP in VGPRs beside the vector work,
+    # dK and dV accumulating in AGPRs through inline assembly (the other
+    # kernels of the file compile to the same code either way)
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

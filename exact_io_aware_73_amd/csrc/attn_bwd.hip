@@ -14,12 +14,12 @@
 //
 // Three kernels:
 //   attn_bwd_rowdot  -- D_i per query row (fp32, into the caller's workspace);
-//   attn_bwd_dkdv    -- one workgroup per 128 keys of a K/V head: its K and V
-//                       rows stay in registers while the Q / dO tiles of every
-//                       query head of the group stream through LDS; dK and dV
-//                       accumulate in registers and are written once (head
-//                       dim 64; at 128 attn_bwd_dkdv_rs splits each 32 keys'
-//                       work over two waves, below);
+//   attn_bwd_dkdv    -- one workgroup per 128 keys of a K/V head (head dim
+//                       64; attn_bwd_dkdv_w64 at 128: 256 keys, 64 per
+//                       wave): the keys' K and V rows stay in registers while
+//                       the Q / dO tiles of every query head of the group
+//                       stream through LDS; dK and dV accumulate in registers
+//                       and are written once;
 //   attn_bwd_dq      -- one workgroup per 128 query rows: the K / V tiles of
 //                       the head stream through LDS (as in the forward) and dQ
 //                       accumulates in registers; no atomics anywhere.
@@ -58,12 +58,12 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
-template <int D>
+template <int D, int R = kTRows>
 struct BGeo {
   static constexpr int kKSteps = D / 16;               // MFMA k-steps over d
   static constexpr int kDB = D / 32;                   // 32-wide d blocks
   static constexpr int kCPR = D / 8;                   // 16-byte chunks per row
-  static constexpr int kTile = kTRows * D;             // bf16 elements of one tile
+  static constexpr int kTile = R * D;                  // bf16 elements of one R-row tile
   static constexpr int kDma = kTile / 8 / kBThreads;   // 16-byte loads per lane per tile
   static_assert(kDma * 8 * kBThreads == kTile, "tile must split over the workgroup");
 };
@@ -83,15 +83,16 @@ __device__ __forceinline__ int srows(int rem, int hi) {
   return r;
 }
 
-// Rows j0 .. j0 + 63 of a [N, D] bf16 array -> the LDS tile at byte address
-// lds_tile, global -> LDS directly.  The buffer covers only rows j0 .. N-1:
-// rows past N read as zeros and nothing is read out of bounds.  Inline
-// assembly, as in the forward: the waits below order it against readers.
-template <int D>
+// Rows j0 .. j0 + R - 1 of a [N, D] bf16 array -> the LDS tile at byte
+// address lds_tile, global -> LDS directly.  The buffer covers only rows
+// j0 .. N-1: rows past N read as zeros and nothing is read out of bounds.
+// Inline assembly, as in the forward: the waits below order it against
+// readers.
+template <int D, int R = kTRows>
 __device__ __forceinline__ void dma_tile(const __bf16* __restrict__ base, int j0, int N,
                                          uint32_t lds_tile, int wave, const int* dvoff) {
-  using G = BGeo<D>;
-  const int rows = srows(N - j0, kTRows);
+  using G = BGeo<D, R>;
+  const int rows = srows(N - j0, R);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<__bf16*>(base) + (int64_t)min(j0, N) * D, (short)0, rows * D * 2, 0x00020000);
 #pragma unroll
@@ -106,18 +107,18 @@ __device__ __forceinline__ void dma_tile(const __bf16* __restrict__ base, int j0
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Per-lane LDS byte offsets of one tile's operand reads.
-template <int D>
+template <int D, int R = kTRows>
 struct TileOffsets {
-  int dvoff[BGeo<D>::kDma];     // this lane's 16-byte chunks of a tile load
+  int dvoff[BGeo<D, R>::kDma];  // this lane's 16-byte chunks of a tile load
   int row[BGeo<D>::kKSteps];    // 16-byte row read: row l32, chunk 2 s + hh
   int tr[BGeo<D>::kDB];         // transposing read, rows +0..3 of a 16-row step
   int tr8[BGeo<D>::kDB];        // the same, rows +8..11
 };
 
-template <int D>
-__device__ __forceinline__ TileOffsets<D> tile_offsets(int lane, int wave) {
-  using G = BGeo<D>;
-  TileOffsets<D> t;
+template <int D, int R = kTRows>
+__device__ __forceinline__ TileOffsets<D, R> tile_offsets(int lane, int wave) {
+  using G = BGeo<D, R>;
+  TileOffsets<D, R> t;
   const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
   for (int i = 0; i < G::kDma; ++i) {
@@ -253,7 +254,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   const int64_t head_q = ((int64_t)b * Hkv + kvh) * (int64_t)n_qrows;
 
   const int krow = kt * kWgRows + wave * kWRows + l32;   // this lane's key (B operand column)
-  static_assert(D == 64, "head dim 128 runs attn_bwd_dkdv_rs_kernel");
+  static_assert(D == 64, "head dim 128 runs attn_bwd_dkdv_w64_kernel");
   bf16x8 kf[G::kKSteps], vf[G::kKSteps];
   load_rowfrags<D>(kf, k + head_kv * D, krow, N, hh);
   load_rowfrags<D>(vf, v + head_kv * D, krow, N, hh);
@@ -366,84 +367,64 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
   }
 }
 
-// acc[qb] = rows qb*32 .. +31 of the LDS tile times the wave's fragments
-// (32 x 32 keys, over d), the row reads issued eight ahead of their products
-// in a fixed order (the compiler otherwise waits on each read right before
-// its product); extra(i), i < 8, is run after the i-th product of the second
-// block (further LDS reads that go with the step).
-template <int D, typename Extra>
-__device__ __forceinline__ void row_products(f32x16 (&acc)[2], uint32_t tile, const TileOffsets<D>& off,
-                                             const bf16x8 (&frag)[BGeo<D>::kKSteps], Extra extra) {
-  constexpr int kS = BGeo<D>::kKSteps;
-  static_assert(kS == 8, "eight k-steps per block");
-  bf16x8 a0[kS], a1[kS];
-#pragma unroll
-  for (int s = 0; s < kS; ++s) a0[s] = lds_row(tile, off.row[s]);
-  __builtin_amdgcn_sched_barrier(0);
-  acc[0] = f32x16{};
-  acc[1] = f32x16{};
-#pragma unroll
-  for (int s = 0; s < kS; ++s) {
-    acc[0] = mfma32x32x16(a0[s], frag[s], acc[0]);
-    a1[s] = lds_row(tile + 32 * D * 2, off.row[s]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int s = 0; s < kS; ++s) {
-    acc[1] = mfma32x32x16(a1[s], frag[s], acc[1]);
-    extra(s);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+// ---------------------------------------------------------------------------
+// acc += a b on the matrix core with the accumulator in AGPRs (the d = 128
+// dK/dV kernel below needs both register files: dK and dV fill the AGPRs,
+// everything else uses VGPRs; the compiler places all accumulators of a
+// kernel in one file).  A matrix-core read of a register the vector ALU
+// wrote needs two wait states in between: kNop when b may have been
+// written within the last two instructions.  Back-to-back products into
+// the same accumulator need none.
+template <bool kNop>
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (kNop)
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// acc = a b, the first product of a chain (the accumulator starts in AGPRs).
+template <bool kNop>
+__device__ __forceinline__ void mfma_agpr_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (kNop)
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
 }
 
-// ---------------------------------------------------------------------------
-// dK and dV at head dim 128: one workgroup of eight waves (two per SIMD) per
-// 128 keys of K/V head (b, kvh), two roles per 32 keys.  Waves 0..3 ("P
-// waves") hold K, compute S = Q K^T and P = exp2(S c - lse), hand P (fp32)
-// to their partner wave through LDS and accumulate dV^T += dO^T P; they also
-// issue the loads.  Waves 4..7 ("dS waves") hold V, take P from LDS, form
-// dS = P (dP - D), accumulate dK^T += Q^T dS and compute dP = dO V^T for
-// the next step.  S is computed once per block (four products; one wave
-// holding K, V, dK and dV would need ~370 registers, one wave per SIMD).
-//
-// In step t the P wave runs query tile t (products, weights, products) and
-// the dS wave finishes tile t - 1 (weights first, then dK) and then forms
-// dP of tile t, so each wave's vector work runs while its partner on the
-// same SIMD issues products.  P goes through two LDS buffers per pair (tile
-// t into buffer t % 2), so one barrier per step orders the hand-over: P(t)
-// is read in step t + 1 and its buffer written again in step t + 2.  LDS
-// slots: Q of tiles t - 1, t and t + 1 (three), dO of tiles t and t + 1
-// (two), lse and D beside each Q slot.
+// dK and dV at head dim 128: one workgroup of four waves (one per SIMD) per
+// 256 keys of K/V head (b, kvh); each wave owns 64 keys (two 32-key blocks)
+// and runs all four products for them: S = Q K^T, dP = dO V^T, then
+// dV^T += dO^T P and dK^T += Q^T dS.  K and V of its keys stay in VGPRs
+// (128), dK and dV in AGPRs (256); every Q / dO operand read from LDS feeds
+// one product per key block, and P stays in registers.  A step covers 32
+// query rows; the next tile loads during the step (two LDS slots).
+constexpr int kW64Keys = 64;                    // keys a wave owns
+constexpr int kW64Rows = 32;                    // query rows per step
+constexpr int kW64WgKeys = kBWaves * kW64Keys;  // keys a workgroup owns
+
 template <int D>
-__global__ __launch_bounds__(2 * kBThreads, 1)
-void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                             const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
-                             const float* __restrict__ lse, const float* __restrict__ dvec,
-                             __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Hq, int Hkv,
-                             int N, float c_log2, float scale, int n_ktiles, uint32_t n_xcd) {
+__global__ __launch_bounds__(kBThreads, 1)
+void attn_bwd_dkdv_w64_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                              const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                              const float* __restrict__ lse, const float* __restrict__ dvec,
+                              __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Hq, int Hkv,
+                              int N, float c_log2, float scale, int n_ktiles, uint32_t n_xcd) {
   static_assert(D == 128, "head dim 64 runs attn_bwd_dkdv_kernel");
-  using G = BGeo<D>;
+  using G = BGeo<D, kW64Rows>;
+  constexpr int kKB = kW64Keys / 32;                         // 32-key blocks per wave
   constexpr uint32_t kTileB = G::kTile * 2;
-  constexpr uint32_t kStatB = 2 * kTRows * 4;                // lse and D of one tile
-  constexpr int kQB = kTRows / 32;
-  constexpr uint32_t kPB = (uint32_t)kWave * kQB * 16 * 4;   // P of one wave-step, fp32
-  constexpr int kNQ = 3, kNO = 2, kNP = 2;                   // Q, dO and P buffers
-  constexpr uint32_t kQOff = 0;
-  constexpr uint32_t kOOff = kQOff + kNQ * kTileB;
-  constexpr uint32_t kSOff = kOOff + kNO * kTileB;
-  constexpr uint32_t kPOff = kSOff + kNQ * kStatB;
-  constexpr uint32_t kPSlot = kBWaves * kPB;
-  __shared__ __align__(16) unsigned char smem[kPOff + kNP * kPSlot];
+  constexpr uint32_t kStatB = 2 * kW64Rows * 4;              // lse and D of one tile
+  constexpr uint32_t kStageB = 2 * kTileB + kStatB;          // Q, dO, lse, D
+  constexpr uint32_t kOutB = kW64Keys * D * 2;               // one wave's dK or dV, bf16
+  constexpr uint32_t kSmem = 2 * kStageB > kBWaves * kOutB ? 2 * kStageB : kBWaves * kOutB;
+  __shared__ __align__(16) unsigned char smem[kSmem];
   const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool is_p = wave8 < kBWaves;
-  const int wave = wave8 & (kBWaves - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const uint32_t pbuf = lds + kPOff + (uint32_t)wave * kPB + (uint32_t)lane * 16;
 
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x, n_xcd);
   const int kt = (int)(logical % (uint32_t)n_ktiles);
@@ -454,162 +435,237 @@ void attn_bwd_dkdv_rs_kernel(const __bf16* __restrict__ q, const __bf16* __restr
   const int n_qrows = (Hq / Hkv) * N;
   const int64_t head_q = ((int64_t)b * Hkv + kvh) * (int64_t)n_qrows;
 
-  const int krow = kt * kWgRows + wave * kWRows + l32;   // this lane's key
-  bf16x8 kvf[G::kKSteps];                                // K (P waves) or V (dS waves)
-  load_rowfrags<D>(kvf, (is_p ? k : v) + head_kv * D, krow, N, hh);
-
-  const TileOffsets<D> off = tile_offsets<D>(lane, wave);
-  f32x16 acc[G::kDB];                                    // dV^T (P waves) or dK^T (dS waves)
+  const int krow0 = kt * kW64WgKeys + wave * kW64Keys + l32;   // this lane's key in block 0
+  bf16x8 kf[kKB][G::kKSteps], vf[kKB][G::kKSteps];
 #pragma unroll
-  for (int i = 0; i < G::kDB; ++i) acc[i] = f32x16{};
+  for (int kb = 0; kb < kKB; ++kb) {
+    load_rowfrags<D>(kf[kb], k + head_kv * D, krow0 + 32 * kb, N, hh);
+    load_rowfrags<D>(vf[kb], v + head_kv * D, krow0 + 32 * kb, N, hh);
+  }
 
-  const int n_steps = (n_qrows + kTRows - 1) / kTRows;
-  // Loads of tile t (P waves): the row statistics first and scaled only
-  // when committed, so no wait for them covers the tile loads.
+  const TileOffsets<D, kW64Rows> off = tile_offsets<D, kW64Rows>(lane, wave);
+  f32x16 dka[kKB][G::kDB], dva[kKB][G::kDB];               // set by the first step
+
+  const int n_steps = (n_qrows + kW64Rows - 1) / kW64Rows;
+  // Loads of tile t: the row statistics first and scaled only when
+  // committed, so no wait for them covers the tile loads.
   float st_lse = 0.0f, st_d = 0.0f;
-  auto issue = [&](int t, uint32_t qslot, uint32_t oslot) {
-    const int q0 = t * kTRows;
-    if (tid < kTRows) {
+  auto issue = [&](int t, uint32_t stage) {
+    const int q0 = t * kW64Rows;
+    if (tid < kW64Rows) {
       const int row = q0 + tid;
       st_lse = row < n_qrows ? lse[head_q + row] : INFINITY;
       st_d = row < n_qrows ? dvec[head_q + row] : 0.0f;
     }
-    dma_tile<D>(q + head_q * D, q0, n_qrows, qslot, wave, off.dvoff);
-    dma_tile<D>(dout + head_q * D, q0, n_qrows, oslot, wave, off.dvoff);
+    dma_tile<D, kW64Rows>(q + head_q * D, q0, n_qrows, stage, wave, off.dvoff);
+    dma_tile<D, kW64Rows>(dout + head_q * D, q0, n_qrows, stage + kTileB, wave, off.dvoff);
   };
-  auto commit = [&](uint32_t sslot) {
-    if (tid < kTRows) {
-      *(__attribute__((address_space(3))) float*)(uintptr_t)(sslot + tid * 4) = st_lse * kLog2e;
-      *(__attribute__((address_space(3))) float*)(uintptr_t)(sslot + kTRows * 4 + tid * 4) = st_d;
+  auto commit = [&](uint32_t stage) {
+    if (tid < kW64Rows) {
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + tid * 4) = st_lse * kLog2e;
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(stage + 2 * kTileB + kW64Rows * 4 + tid * 4) = st_d;
     }
   };
+  // Per-lane LDS offsets.  The tile swizzle is an XOR on the 16-byte chunk
+  // index, so k-step s of a row read sits at row0 ^ 32 s and d block db of
+  // a transposing read at tr0 ^ 64 db (rows +0..3) and its ^ 128, + 2048
+  // (rows +8..11): two registers instead of sixteen, one XOR per read.
+  int row0 = off.row[0], tr0 = off.tr[0];
+  auto R = [&](uint32_t tile, int s) { return lds_row(tile, row0 ^ (32 * s)); };
+  auto T = [&](uint32_t tile, int s2, int db) {
+    const int lo = tr0 ^ (64 * db);
+    return lds_tr(tile + (uint32_t)(16 * s2 * D * 2), lo, (lo ^ 128) + 2048);
+  };
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-  if (is_p) issue(0, lds + kQOff, lds + kOOff);
-  // every wave: its K or V fragments, and (P waves) tile 0, have landed
+  issue(0, lds);
+  // K, V and tile 0 have landed
   wait_vm();
-  if (is_p) commit(lds + kSOff);
+  commit(lds);
   __syncthreads();
 
-  // Slots of step t are compile-time constants: the loops below run six
-  // steps per trip (the buffer counts 3 and 2 divide 6), c = t % 6.
-  auto p_step = [&](const int t, auto c_) {
-    constexpr int c = decltype(c_)::value;
-    constexpr uint32_t qs = kQOff + (uint32_t)(c % kNQ) * kTileB;
-    constexpr uint32_t os = kOOff + (uint32_t)(c % kNO) * kTileB;
-    constexpr uint32_t ss = kSOff + (uint32_t)(c % kNQ) * kStatB;
-    constexpr uint32_t ps = (uint32_t)(c % kNP) * kPSlot;
+  // One query tile per step, stage t % 2 (a compile-time constant: the loop
+  // runs two steps per trip).  The step's instructions are placed in a
+  // fixed order (fences between groups) so that each product's operand is
+  // read two products ahead and the vector work runs between the products
+  // that do not depend on it:
+  //   1. S = Q K^T                      (16 products)
+  //   2. dP = dO V^T, and P = exp2(S c - lse) in place   (16 products)
+  //   3. dV^T += dO^T P, and dS = P (dP - D) packed      (16 products)
+  //   4. dK^T += Q^T dS                                  (16 products)
+  auto step = [&](const int t, auto stage_c, auto first_c) {
+    constexpr int st = decltype(stage_c)::value;
+    constexpr bool first = decltype(first_c)::value;
+    const uint32_t stage = lds + (uint32_t)st * kStageB;
+    const uint32_t qtile = stage, dotile = stage + kTileB;
+    const uint32_t lse_s = stage + 2 * kTileB, d_s = lse_s + kW64Rows * 4;
     const bool more = t + 1 < n_steps;
-    if (more)
-      issue(t + 1, lds + kQOff + (uint32_t)((c + 1) % kNQ) * kTileB,
-            lds + kOOff + (uint32_t)((c + 1) % kNO) * kTileB);
-    if (t < n_steps) {
-      const uint32_t qtile = lds + qs, dotile = lds + os;
-      f32x4 l4v[kQB][4];
-      f32x16 sacc[kQB];
-      row_products<D>(sacc, qtile, off, kvf, [&](int i) {
-        l4v[i / 4][i % 4] = *(const lds_f32x4*)(uintptr_t)(lds + ss + ((i / 4) * 32 + 8 * (i % 4) + 4 * hh) * 4);
-      });
+    if (more) issue(t + 1, lds + (uint32_t)(1 - st) * kStageB);
+    // recomputed each step, not kept as sixteen loop-invariant registers
+    asm volatile("" : "+v"(row0), "+v"(tr0));
+    fence();
+    f32x16 sacc[kKB], pacc[kKB];
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        float p[16];
+    for (int kb = 0; kb < kKB; ++kb) sacc[kb] = pacc[kb] = f32x16{};
+    // 1. S
+    bf16x8 a[G::kKSteps];
+    a[0] = R(qtile, 0);
+    a[1] = R(qtile, 1);
+    fence();
+    f32x4 l4[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // element 4 r + j: query qb*32 + 8 r + 4 hh + j
-          const f32x4 l4 = l4v[qb][r];
-          f32x4 pv;
+    for (int s = 0; s < G::kKSteps; ++s) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p[4 * r + j] = exp2_fast(__builtin_fmaf(sacc[qb][4 * r + j], c_log2, -l4[j]));
-            pv[j] = p[4 * r + j];
-          }
-          *(lds_f32x4*)(uintptr_t)(pbuf + ps + (uint32_t)(qb * 4 + r) * kWave * 16) = pv;
+      for (int kb = 0; kb < kKB; ++kb) sacc[kb] = mfma32x32x16(a[s], kf[kb][s], sacc[kb]);
+      if (s + 2 < G::kKSteps) a[s + 2] = R(qtile, s + 2);
+      else a[s + 2 - G::kKSteps] = R(dotile, s + 2 - G::kKSteps);
+      if (s == 4) l4[0] = *(const lds_f32x4*)(uintptr_t)(lse_s + 4 * hh * 4);
+      if (s == 5) l4[1] = *(const lds_f32x4*)(uintptr_t)(lse_s + (8 + 4 * hh) * 4);
+      fence();
+    }
+    // 2. dP, with the weights of block kb = s % 2, rows r = s / 2 (lse of
+    // rows r read two groups ahead) and the bf16 packing of rows 0 and 1 in
+    // groups 4 .. 7: half of a group's vector work after each of its two
+    // products, so it issues while the product runs (a second product
+    // right behind the first would hold the wave until the first is done)
+    f32x4 d4[4];
+    u32x4 pu[2][kKB];
+#pragma unroll
+    for (int s = 0; s < G::kKSteps; ++s) {
+      const int r = s / 2, kb = s % 2;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        pacc[h] = mfma32x32x16(a[s], vf[h][s], pacc[h]);
+        fence();
+#pragma unroll
+        for (int j = 2 * h; j < 2 * h + 2; ++j)
+          sacc[kb][4 * r + j] = exp2_fast(__builtin_fmaf(sacc[kb][4 * r + j], c_log2, -l4[r][j]));
+        if (s >= 4) {
+          const int pk = s - 4;                          // block pk / 2, word 2 (pk % 2) + h
+          const int w = 2 * (pk % 2) + h;
+          pu[0][pk / 2][w] = pack_bf16x2(sacc[pk / 2][2 * w], sacc[pk / 2][2 * w + 1]);
         }
-        // dV^T += dO^T P over the two 16-query k-steps of the block
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          u32x4 pu;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) pu[w] = pack_bf16x2(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
-          const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
-#pragma unroll
-          for (int db = 0; db < G::kDB; ++db)
-            acc[db] = mfma32x32x16(lds_tr(dotile + rb, off.tr[db], off.tr8[db]), as_bf16x8(pu), acc[db]);
+        if (h == 1) {
+          if (s + 2 < G::kKSteps) a[s + 2] = R(dotile, s + 2);
+          if (kb == 0 && r + 2 < 4) l4[r + 2] = *(const lds_f32x4*)(uintptr_t)(lse_s + (8 * (r + 2) + 4 * hh) * 4);
+          if (s == 6) d4[0] = *(const lds_f32x4*)(uintptr_t)(d_s + 4 * hh * 4);
+          if (s == 7) d4[1] = *(const lds_f32x4*)(uintptr_t)(d_s + (8 + 4 * hh) * 4);
         }
+        fence();
       }
+    }
+    // 3. dV, with dS of rows r = g / 2, block kb = g % 2 in group g, split
+    // over the group's two products as above
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        pu[1][kb][w] = pack_bf16x2(sacc[kb][8 + 2 * w], sacc[kb][8 + 2 * w + 1]);
+    bf16x8 tb[2];
+    tb[0] = T(dotile, 0, 0);
+    tb[1] = T(dotile, 0, 1);
+    fence();
+    u32x4 du[2][kKB];
+#pragma unroll
+    for (int g = 0; g < 2 * G::kDB; ++g) {
+      const int s2 = g / G::kDB, db = g % G::kDB;
+      const int r = g / 2, kb = g % 2;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // only the first product follows the packing of P closely
+        if (first && s2 == 0) {
+          if (g == 0 && h == 0) mfma_agpr_first<true>(dva[h][db], tb[g % 2], as_bf16x8(pu[s2][h]));
+          else mfma_agpr_first<false>(dva[h][db], tb[g % 2], as_bf16x8(pu[s2][h]));
+        } else {
+          if (g == 0 && h == 0) mfma_agpr<true>(dva[h][db], tb[g % 2], as_bf16x8(pu[s2][h]));
+          else mfma_agpr<false>(dva[h][db], tb[g % 2], as_bf16x8(pu[s2][h]));
+        }
+        fence();
+        if (h == 0 && kb == 0 && r + 2 < 4) d4[r + 2] = *(const lds_f32x4*)(uintptr_t)(d_s + (8 * (r + 2) + 4 * hh) * 4);
+        float ds[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) ds[j] = sacc[kb][4 * r + 2 * h + j] * (pacc[kb][4 * r + 2 * h + j] - d4[r][2 * h + j]);
+        // rows r = 2 s2' + q: packed word 2 q + h of du[s2'][kb]
+        du[r / 2][kb][2 * (r % 2) + h] = pack_bf16x2(ds[0], ds[1]);
+        if (h == 1) {
+          if (g + 2 < 2 * G::kDB) tb[g % 2] = T(dotile, (g + 2) / G::kDB, (g + 2) % G::kDB);
+          else tb[g % 2] = T(qtile, (g + 2 - 2 * G::kDB) / G::kDB, (g + 2 - 2 * G::kDB) % G::kDB);
+        }
+        fence();
+      }
+    }
+    // 4. dK (each dS word was packed at least four products before its
+    // first use)
+#pragma unroll
+    for (int g = 0; g < 2 * G::kDB; ++g) {
+      const int s2 = g / G::kDB, db = g % G::kDB;
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) {
+        if (first && s2 == 0) mfma_agpr_first<false>(dka[kb][db], tb[g % 2], as_bf16x8(du[s2][kb]));
+        else mfma_agpr<false>(dka[kb][db], tb[g % 2], as_bf16x8(du[s2][kb]));
+      }
+      if (g + 2 < 2 * G::kDB) tb[g % 2] = T(qtile, (g + 2) / G::kDB, (g + 2) % G::kDB);
+      fence();
     }
     // unconditional: the compiler then knows no load is in flight at the
     // next step's start (else it waits for the next tile's loads there)
     wait_vm();
-    if (more) commit(lds + kSOff + (uint32_t)((c + 1) % kNQ) * kStatB);
+    if (more) commit(lds + (uint32_t)(1 - st) * kStageB);
     __syncthreads();
   };
-  f32x16 pacc[kQB];                                      // dP of the dS wave's next tile
-  auto ds_step = [&](const int t, auto c_) {
-    constexpr int c = decltype(c_)::value;
-    constexpr int cp = (c + 5) % 6;                      // (t - 1) % 6
-    constexpr uint32_t qs = kQOff + (uint32_t)(cp % kNQ) * kTileB;
-    constexpr uint32_t ds_off = kSOff + (uint32_t)(cp % kNQ) * kStatB + kTRows * 4;
-    constexpr uint32_t ps = (uint32_t)(cp % kNP) * kPSlot;
-    constexpr uint32_t os = kOOff + (uint32_t)(c % kNO) * kTileB;
-    if (t > 0) {
-      // tile t - 1: P written by the partner last step, D of its rows, dP
-      // from last step
-      const uint32_t qtile = lds + qs;
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        f32x4 pv[4], d4v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pv[r] = *(const lds_f32x4*)(uintptr_t)(pbuf + ps + (uint32_t)(qb * 4 + r) * kWave * 16);
-          d4v[r] = *(const lds_f32x4*)(uintptr_t)(lds + ds_off + (qb * 32 + 8 * r + 4 * hh) * 4);
-        }
-        float ds[16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) ds[4 * r + j] = pv[r][j] * (pacc[qb][4 * r + j] - d4v[r][j]);
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          u32x4 du;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) du[w] = pack_bf16x2(ds[8 * s2 + 2 * w], ds[8 * s2 + 2 * w + 1]);
-          const uint32_t rb = (uint32_t)((qb * 32 + 16 * s2) * D * 2);
-#pragma unroll
-          for (int db = 0; db < G::kDB; ++db)
-            acc[db] = mfma32x32x16(lds_tr(qtile + rb, off.tr[db], off.tr8[db]), as_bf16x8(du), acc[db]);
-        }
-      }
-    }
-    if (t < n_steps) {
-      // dP = dO V^T of tile t, used next step
-      row_products<D>(pacc, lds + os, off, kvf, [](int) {});
-    }
-    __syncthreads();
-  };
-  if (is_p) {
-    for (int t = 0; t <= n_steps; t += 6) {
-      p_step(t, std::integral_constant<int, 0>{});
-      if (t + 1 <= n_steps) p_step(t + 1, std::integral_constant<int, 1>{});
-      if (t + 2 <= n_steps) p_step(t + 2, std::integral_constant<int, 2>{});
-      if (t + 3 <= n_steps) p_step(t + 3, std::integral_constant<int, 3>{});
-      if (t + 4 <= n_steps) p_step(t + 4, std::integral_constant<int, 4>{});
-      if (t + 5 <= n_steps) p_step(t + 5, std::integral_constant<int, 5>{});
-    }
-  } else {
-    for (int t = 0; t <= n_steps; t += 6) {
-      ds_step(t, std::integral_constant<int, 0>{});
-      if (t + 1 <= n_steps) ds_step(t + 1, std::integral_constant<int, 1>{});
-      if (t + 2 <= n_steps) ds_step(t + 2, std::integral_constant<int, 2>{});
-      if (t + 3 <= n_steps) ds_step(t + 3, std::integral_constant<int, 3>{});
-      if (t + 4 <= n_steps) ds_step(t + 4, std::integral_constant<int, 4>{});
-      if (t + 5 <= n_steps) ds_step(t + 5, std::integral_constant<int, 5>{});
-    }
+  step(0, std::integral_constant<int, 0>{}, std::true_type{});
+  for (int t = 1; t < n_steps; t += 2) {
+    step(t, std::integral_constant<int, 1>{}, std::false_type{});
+    if (t + 1 < n_steps) step(t + 1, std::integral_constant<int, 0>{}, std::false_type{});
   }
 
-  if (krow < N) {
-    if (is_p) store_rowT<D>(acc, dv + (head_kv + krow) * D, 1.0f, hh);
-    else store_rowT<D>(acc, dk + (head_kv + krow) * D, scale, hh);
-  }
+  // The compiler does not see the products above as matrix-core work:
+  // wait out their write latency (18 wait states) before the accumulators
+  // are read, each accumulator passing through an (empty) statement ordered
+  // after the wait.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+    for (int i = 0; i < G::kDB; ++i) {
+      asm volatile("" : "+a"(dka[kb][i]));
+      asm volatile("" : "+a"(dva[kb][i]));
+    }
+  // dV, then dK, through LDS: the accumulators hold four consecutive d of a
+  // row per lane, so direct stores would complete each 256-byte row with 16
+  // partial writes, and with 128 KB of output per workgroup the L2 evicts
+  // lines before they are whole (measured: 2.3x the bytes).  Each wave
+  // writes its 64 rows to its own 16 KB of LDS (16-byte chunks XOR-swizzled
+  // by row), then stores whole rows, 16 lanes per row.  The last step's
+  // barrier has freed the tile stages; one wave's LDS accesses stay in
+  // order, so dK may overwrite dV's rows once they are read.
+  const uint32_t wout = lds + (uint32_t)wave * kOutB;
+  auto store_out = [&](f32x16 (&acc)[kKB][G::kDB], float mul, __bf16* __restrict__ out) {
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int db = 0; db < G::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // key 32 kb + l32, d = 32 db + 8 r + 4 hh .. + 3: 16-byte chunk 4 db + r
+          const int row = 32 * kb + l32;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[kb][db][4 * r + 0] * mul, acc[kb][db][4 * r + 1] * mul);
+          w[1] = pack_bf16x2(acc[kb][db][4 * r + 2] * mul, acc[kb][db][4 * r + 3] * mul);
+          *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(
+              wout + (uint32_t)(row * D * 2 + (((4 * db + r) ^ (row & 15)) * 16) + hh * 8)) = w;
+        }
+    const int c = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kW64Keys / 4; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      const u32x4 v16 = *(const lds_u32x4*)(uintptr_t)(wout + (uint32_t)(row * D * 2 + ((c ^ (row & 15)) * 16)));
+      const int key = kt * kW64WgKeys + wave * kW64Keys + row;
+      if (key < N) *reinterpret_cast<u32x4*>(out + (head_kv + key) * D + c * 8) = v16;
+    }
+  };
+  store_out(dva, 1.0f, dv);
+  store_out(dka, scale, dk);
 }
 
 // ---------------------------------------------------------------------------
@@ -732,11 +788,13 @@ hipError_t launch_d(const FwdArgs& a, const BwdArgs& g) {
                      n_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_kt = (a.N + kWgRows - 1) / kWgRows;
+  // head dim 128: one wave per 64 keys (attn_bwd_dkdv_w64_kernel); 64: one
+  // wave per 32 keys
+  const int wg_keys = D == 128 ? kW64WgKeys : kWgRows;
+  const int n_kt = (a.N + wg_keys - 1) / wg_keys;
   const uint64_t grid1 = (uint64_t)n_kt * a.Hkv * a.B;
-  // head dim 128: two waves per 32 keys (attn_bwd_dkdv_rs_kernel); 64: one
   if constexpr (D == 128) {
-    hipLaunchKernelGGL((attn_bwd_dkdv_rs_kernel<D>), dim3((uint32_t)grid1), dim3(2 * kBThreads), 0,
+    hipLaunchKernelGGL((attn_bwd_dkdv_w64_kernel<D>), dim3((uint32_t)grid1), dim3(kBThreads), 0,
                        a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                        static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(g.dout), a.lse,
                        g.dvec, static_cast<__bf16*>(g.dk), static_cast<__bf16*>(g.dv), a.Hq, a.Hkv,
