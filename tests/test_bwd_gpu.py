@@ -52,7 +52,9 @@ def _inputs(B, Hq, Hkv, N, d, seed):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [1, 17, 64, 65, 127, 128, 129, 300])
+# 300, 400, 520: several dK/dV workgroups (256 keys each at d = 128), the
+# last one with whole, partial and empty waves and key blocks
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 127, 128, 129, 300, 400, 520])
 @pytest.mark.parametrize("B,Hq,Hkv", [(1, 1, 1), (2, 4, 2)])
 def test_bwd_small(attn, B, Hq, Hkv, N, d):
     q, k, v, do = _inputs(B, Hq, Hkv, N, d, 31 * N + d + Hq)
