@@ -391,13 +391,14 @@ __device__ __forceinline__ void mfma_agpr_first(f32x16& acc, const bf16x8& a, co
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
 }
 
-// dK and dV at head dim 128: one workgroup of four waves (one per SIMD) per
-// 256 keys of K/V head (b, kvh); each wave owns 64 keys (two 32-key blocks)
-// and runs all four products for them: S = Q K^T, dP = dO V^T, then
-// dV^T += dO^T P and dK^T += Q^T dS.  K and V of its keys stay in VGPRs
-// (128), dK and dV in AGPRs (256); every Q / dO operand read from LDS feeds
-// one product per key block, and P stays in registers.  A step covers 32
-// query rows; the next tile loads during the step (two LDS slots).
+// dK and dV at head dim 128 (written for 64 and 128; launched at 128): one
+// workgroup of four waves (one per SIMD) per 256 keys of K/V head (b, kvh);
+// each wave owns 64 keys (two 32-key blocks) and runs all four products for
+// them: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.  K
+// and V of its keys stay in VGPRs (128 at d = 128), dK and dV in AGPRs
+// (256); every Q / dO operand read from LDS feeds one product per key
+// block, and P stays in registers.  A step covers 32 query rows; the next
+// tile loads during the step (two LDS slots).
 constexpr int kW64Keys = 64;                    // keys a wave owns
 constexpr int kW64Rows = 32;                    // query rows per step
 constexpr int kW64WgKeys = kBWaves * kW64Keys;  // keys a workgroup owns
@@ -409,9 +410,12 @@ void attn_bwd_dkdv_w64_kernel(const __bf16* __restrict__ q, const __bf16* __rest
                               const float* __restrict__ lse, const float* __restrict__ dvec,
                               __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Hq, int Hkv,
                               int N, float c_log2, float scale, int n_ktiles, uint32_t n_xcd) {
-  static_assert(D == 128, "head dim 64 runs attn_bwd_dkdv_kernel");
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
   using G = BGeo<D, kW64Rows>;
   constexpr int kKB = kW64Keys / 32;                         // 32-key blocks per wave
+  constexpr int kNS = 2 * G::kKSteps;                        // vector slots of phases 2 and 3
+  constexpr int kEPS = 32 / kNS;                             // values per slot: 2 (d = 128), 4
+  static_assert(kNS == 4 * G::kDB && kEPS % 2 == 0, "slot layout");
   constexpr uint32_t kTileB = G::kTile * 2;
   constexpr uint32_t kStatB = 2 * kW64Rows * 4;              // lse and D of one tile
   constexpr uint32_t kStageB = 2 * kTileB + kStatB;          // Q, dO, lse, D
@@ -468,13 +472,15 @@ void attn_bwd_dkdv_w64_kernel(const __bf16* __restrict__ q, const __bf16* __rest
   };
   // Per-lane LDS offsets.  The tile swizzle is an XOR on the 16-byte chunk
   // index, so k-step s of a row read sits at row0 ^ 32 s and d block db of
-  // a transposing read at tr0 ^ 64 db (rows +0..3) and its ^ 128, + 2048
-  // (rows +8..11): two registers instead of sixteen, one XOR per read.
+  // a transposing read at tr0 ^ 64 db (rows +0..3) and its ^ kTrX, + 16 D
+  // (rows +8..11: one more swizzle bit): two registers instead of up to
+  // sixteen, one XOR per read.
+  constexpr int kTrX = D == 128 ? 128 : 16;
   int row0 = off.row[0], tr0 = off.tr[0];
   auto R = [&](uint32_t tile, int s) { return lds_row(tile, row0 ^ (32 * s)); };
   auto T = [&](uint32_t tile, int s2, int db) {
     const int lo = tr0 ^ (64 * db);
-    return lds_tr(tile + (uint32_t)(16 * s2 * D * 2), lo, (lo ^ 128) + 2048);
+    return lds_tr(tile + (uint32_t)(16 * s2 * D * 2), lo, (lo ^ kTrX) + 16 * D);
   };
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
@@ -519,43 +525,51 @@ void attn_bwd_dkdv_w64_kernel(const __bf16* __restrict__ q, const __bf16* __rest
       for (int kb = 0; kb < kKB; ++kb) sacc[kb] = mfma32x32x16(a[s], kf[kb][s], sacc[kb]);
       if (s + 2 < G::kKSteps) a[s + 2] = R(qtile, s + 2);
       else a[s + 2 - G::kKSteps] = R(dotile, s + 2 - G::kKSteps);
-      if (s == 4) l4[0] = *(const lds_f32x4*)(uintptr_t)(lse_s + 4 * hh * 4);
-      if (s == 5) l4[1] = *(const lds_f32x4*)(uintptr_t)(lse_s + (8 + 4 * hh) * 4);
+      if (s == G::kKSteps - 4) l4[0] = *(const lds_f32x4*)(uintptr_t)(lse_s + 4 * hh * 4);
+      if (s == G::kKSteps - 3) l4[1] = *(const lds_f32x4*)(uintptr_t)(lse_s + (8 + 4 * hh) * 4);
       fence();
     }
-    // 2. dP, with the weights of block kb = s % 2, rows r = s / 2 (lse of
-    // rows r read two groups ahead) and the bf16 packing of rows 0 and 1 in
-    // groups 4 .. 7: half of a group's vector work after each of its two
-    // products, so it issues while the product runs (a second product
-    // right behind the first would hold the wave until the first is done)
+    // 2. dP, with the weights P = exp2(S c - lse) in place (lse of rows r
+    // read two units ahead) and the bf16 packing of rows 0 and 1 in the
+    // second half: after each product a slot of vector work, so it issues
+    // while the product runs (a second product right behind the first would
+    // hold the wave until the first is done).  Slot i takes the kEPS values
+    // e = i kEPS .. of the 32 a lane holds: block kb = (e / 4) % 2, rows
+    // r = e / 8 (8 r + 4 hh + e % 4 of the tile).
     f32x4 d4[4];
     u32x4 pu[2][kKB];
 #pragma unroll
     for (int s = 0; s < G::kKSteps; ++s) {
-      const int r = s / 2, kb = s % 2;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        const int i = 2 * s + h;
         pacc[h] = mfma32x32x16(a[s], vf[h][s], pacc[h]);
         fence();
 #pragma unroll
-        for (int j = 2 * h; j < 2 * h + 2; ++j)
+        for (int k = 0; k < kEPS; ++k) {
+          const int e = i * kEPS + k, r = e / 8, kb = (e / 4) % 2, j = e % 4;
           sacc[kb][4 * r + j] = exp2_fast(__builtin_fmaf(sacc[kb][4 * r + j], c_log2, -l4[r][j]));
-        if (s >= 4) {
-          const int pk = s - 4;                          // block pk / 2, word 2 (pk % 2) + h
-          const int w = 2 * (pk % 2) + h;
-          pu[0][pk / 2][w] = pack_bf16x2(sacc[pk / 2][2 * w], sacc[pk / 2][2 * w + 1]);
+        }
+        if (i >= kNS / 2) {
+#pragma unroll
+          for (int k = 0; k < 16 / kNS; ++k) {
+            const int wi = (i - kNS / 2) * (16 / kNS) + k, kb = wi / 4, w = wi % 4;
+            pu[0][kb][w] = pack_bf16x2(sacc[kb][2 * w], sacc[kb][2 * w + 1]);
+          }
+        }
+        {
+          const int e0 = i * kEPS, r = e0 / 8;
+          if (e0 % 8 == 0 && r + 2 < 4) l4[r + 2] = *(const lds_f32x4*)(uintptr_t)(lse_s + (8 * (r + 2) + 4 * hh) * 4);
         }
         if (h == 1) {
           if (s + 2 < G::kKSteps) a[s + 2] = R(dotile, s + 2);
-          if (kb == 0 && r + 2 < 4) l4[r + 2] = *(const lds_f32x4*)(uintptr_t)(lse_s + (8 * (r + 2) + 4 * hh) * 4);
-          if (s == 6) d4[0] = *(const lds_f32x4*)(uintptr_t)(d_s + 4 * hh * 4);
-          if (s == 7) d4[1] = *(const lds_f32x4*)(uintptr_t)(d_s + (8 + 4 * hh) * 4);
+          if (s == G::kKSteps - 2) d4[0] = *(const lds_f32x4*)(uintptr_t)(d_s + 4 * hh * 4);
+          if (s == G::kKSteps - 1) d4[1] = *(const lds_f32x4*)(uintptr_t)(d_s + (8 + 4 * hh) * 4);
         }
         fence();
       }
     }
-    // 3. dV, with dS of rows r = g / 2, block kb = g % 2 in group g, split
-    // over the group's two products as above
+    // 3. dV, with dS = P (dP - D) formed and packed in slots as above
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
@@ -569,9 +583,9 @@ void attn_bwd_dkdv_w64_kernel(const __bf16* __restrict__ q, const __bf16* __rest
 #pragma unroll
     for (int g = 0; g < 2 * G::kDB; ++g) {
       const int s2 = g / G::kDB, db = g % G::kDB;
-      const int r = g / 2, kb = g % 2;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        const int i = 2 * g + h;
         // only the first product follows the packing of P closely
         if (first && s2 == 0) {
           if (g == 0 && h == 0) mfma_agpr_first<true>(dva[h][db], tb[g % 2], as_bf16x8(pu[s2][h]));
@@ -581,12 +595,18 @@ void attn_bwd_dkdv_w64_kernel(const __bf16* __restrict__ q, const __bf16* __rest
           else mfma_agpr<false>(dva[h][db], tb[g % 2], as_bf16x8(pu[s2][h]));
         }
         fence();
-        if (h == 0 && kb == 0 && r + 2 < 4) d4[r + 2] = *(const lds_f32x4*)(uintptr_t)(d_s + (8 * (r + 2) + 4 * hh) * 4);
-        float ds[2];
+        {
+          const int e0 = i * kEPS, r = e0 / 8;
+          if (e0 % 8 == 0 && r + 2 < 4) d4[r + 2] = *(const lds_f32x4*)(uintptr_t)(d_s + (8 * (r + 2) + 4 * hh) * 4);
+        }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) ds[j] = sacc[kb][4 * r + 2 * h + j] * (pacc[kb][4 * r + 2 * h + j] - d4[r][2 * h + j]);
-        // rows r = 2 s2' + q: packed word 2 q + h of du[s2'][kb]
-        du[r / 2][kb][2 * (r % 2) + h] = pack_bf16x2(ds[0], ds[1]);
+        for (int k = 0; k < kEPS; k += 2) {
+          const int e = i * kEPS + k, r = e / 8, kb = (e / 4) % 2, j = e % 4;
+          const float ds0 = sacc[kb][4 * r + j] * (pacc[kb][4 * r + j] - d4[r][j]);
+          const float ds1 = sacc[kb][4 * r + j + 1] * (pacc[kb][4 * r + j + 1] - d4[r][j + 1]);
+          // rows r = 2 s2' + q: packed word 2 q + j / 2 of du[s2'][kb]
+          du[r / 2][kb][2 * (r % 2) + j / 2] = pack_bf16x2(ds0, ds1);
+        }
         if (h == 1) {
           if (g + 2 < 2 * G::kDB) tb[g % 2] = T(dotile, (g + 2) / G::kDB, (g + 2) % G::kDB);
           else tb[g % 2] = T(qtile, (g + 2 - 2 * G::kDB) / G::kDB, (g + 2 - 2 * G::kDB) % G::kDB);
@@ -636,7 +656,7 @@ void attn_bwd_dkdv_w64_kernel(const __bf16* __restrict__ q, const __bf16* __rest
   // partial writes, and with 128 KB of output per workgroup the L2 evicts
   // lines before they are whole (measured: 2.3x the bytes).  Each wave
   // writes its 64 rows to its own 16 KB of LDS (16-byte chunks XOR-swizzled
-  // by row), then stores whole rows, 16 lanes per row.  The last step's
+  // by row), then stores whole rows, D / 8 lanes per row.  The last step's
   // barrier has freed the tile stages; one wave's LDS accesses stay in
   // order, so dK may overwrite dV's rows once they are read.
   const uint32_t wout = lds + (uint32_t)wave * kOutB;
@@ -653,13 +673,13 @@ void attn_bwd_dkdv_w64_kernel(const __bf16* __restrict__ q, const __bf16* __rest
           w[0] = pack_bf16x2(acc[kb][db][4 * r + 0] * mul, acc[kb][db][4 * r + 1] * mul);
           w[1] = pack_bf16x2(acc[kb][db][4 * r + 2] * mul, acc[kb][db][4 * r + 3] * mul);
           *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(
-              wout + (uint32_t)(row * D * 2 + (((4 * db + r) ^ (row & 15)) * 16) + hh * 8)) = w;
+              wout + (uint32_t)(row * D * 2 + (((4 * db + r) ^ (row & (G::kCPR - 1))) * 16) + hh * 8)) = w;
         }
-    const int c = lane & 15;
+    const int c = lane % G::kCPR;
 #pragma unroll
-    for (int i = 0; i < kW64Keys / 4; ++i) {
-      const int row = 4 * i + (lane >> 4);
-      const u32x4 v16 = *(const lds_u32x4*)(uintptr_t)(wout + (uint32_t)(row * D * 2 + ((c ^ (row & 15)) * 16)));
+    for (int i = 0; i < kW64Keys * G::kCPR / kWave; ++i) {
+      const int row = (kWave / G::kCPR) * i + lane / G::kCPR;
+      const u32x4 v16 = *(const lds_u32x4*)(uintptr_t)(wout + (uint32_t)(row * D * 2 + ((c ^ (row & (G::kCPR - 1))) * 16)));
       const int key = kt * kW64WgKeys + wave * kW64Keys + row;
       if (key < N) *reinterpret_cast<u32x4*>(out + (head_kv + key) * D + c * 8) = v16;
     }
@@ -788,8 +808,10 @@ hipError_t launch_d(const FwdArgs& a, const BwdArgs& g) {
                      n_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // head dim 128: one wave per 64 keys (attn_bwd_dkdv_w64_kernel); 64: one
-  // wave per 32 keys
+  // head dim 128: one wave per 64 keys (attn_bwd_dkdv_w64_kernel); 64: two
+  // waves per SIMD of 32 keys each (attn_bwd_dkdv_kernel: the one-wave form
+  // ran 4 % slower there, its step bound by vector work that a second wave
+  // no longer hides)
   const int wg_keys = D == 128 ? kW64WgKeys : kWgRows;
   const int n_kt = (a.N + wg_keys - 1) / wg_keys;
   const uint64_t grid1 = (uint64_t)n_kt * a.Hkv * a.B;
