@@ -275,8 +275,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return ATTN_ERR_ALIGN;
   const uint64_t rows = (uint64_t)B * Hq * N;
-  if (attn::bwd_grid(B, Hq, Hkv, N) > kMaxWorkgroups || rows * 8 / 256 + 1 > kMaxWorkgroups)
-    return ATTN_ERR_SHAPE;
+  if (attn::bwd_grid(B, Hq, Hkv, N) > kMaxWorkgroups) return ATTN_ERR_SHAPE;
   const uint64_t need = rows * 4;
   if (noalloc) {
     if (need > attn::kScratchBytes) return ATTN_ERR_SCRATCH;

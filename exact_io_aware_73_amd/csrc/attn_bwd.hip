@@ -12,17 +12,18 @@
 //   dQ = scale * dS K,   dK = scale * dS^T Q
 // (D_i = sum_j P_ij dP_ij, the row sum the softmax Jacobian subtracts).
 //
-// Three kernels:
-//   attn_bwd_rowdot  -- D_i per query row (fp32, into the caller's workspace);
+// Two kernels, in this order:
+//   attn_bwd_dq      -- one workgroup per 256 query rows: the K / V tiles of
+//                       the head stream through LDS (as in the forward) and dQ
+//                       accumulates in registers; each row's D_i (fp32, from
+//                       the dO rows it holds and O) goes to the caller's
+//                       workspace;
 //   attn_bwd_dkdv    -- one workgroup per 128 keys of a K/V head (head dim
 //                       64; attn_bwd_dkdv_w64 at 128: 256 keys, 64 per
 //                       wave): the keys' K and V rows stay in registers while
-//                       the Q / dO tiles of every query head of the group
-//                       stream through LDS; dK and dV accumulate in registers
-//                       and are written once;
-//   attn_bwd_dq      -- one workgroup per 256 query rows: the K / V tiles of
-//                       the head stream through LDS (as in the forward) and dQ
-//                       accumulates in registers; no atomics anywhere.
+//                       the Q / dO tiles (and lse, D) of every query head of
+//                       the group stream through LDS; dK and dV accumulate in
+//                       registers and are written once; no atomics anywhere.
 // S and dP are computed twice (once per kernel): 7 products per (query, key)
 // block instead of 5, traded for no atomic adds and no [N, N] storage.
 //
@@ -184,37 +185,6 @@ __device__ __forceinline__ void store_rowT(const f32x16 (&acc)[BGeo<D>::kDB], __
       w[1] = pack_bf16x2(acc[db][4 * r + 2] * mul, acc[db][4 * r + 3] * mul);
       *reinterpret_cast<u32x2*>(out + db * 32 + 8 * r + 4 * hh) = w;
     }
-}
-
-// ---------------------------------------------------------------------------
-// D_i = sum_c dO[i, c] * O[i, c]: eight lanes per row, fp32.
-template <int D>
-__global__ __launch_bounds__(256)
-void attn_bwd_rowdot_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                            float* __restrict__ dvec, int64_t n_rows) {
-  constexpr int kPer = D / 8;   // elements per lane
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = t >> 3;
-  const int sub = (int)(t & 7);
-  float acc = 0.0f;
-  if (row < n_rows) {
-    const __bf16* po = o + row * D + sub * kPer;
-    const __bf16* pd = dout + row * D + sub * kPer;
-#pragma unroll
-    for (int c = 0; c < kPer; c += 8) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(po + c);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(pd + c);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc = __builtin_fmaf(bf16_bits_to_float(a[w] & 0xFFFFu), bf16_bits_to_float(b[w] & 0xFFFFu), acc);
-        acc = __builtin_fmaf(bf16_bits_to_float(a[w] >> 16), bf16_bits_to_float(b[w] >> 16), acc);
-      }
-    }
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
-  if (row < n_rows && sub == 0) dvec[row] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -703,8 +673,9 @@ constexpr int kDqTRows = D == 128 ? kTRows : 2 * kTRows;
 template <int D, int kW, int R>
 __global__ __launch_bounds__(kW * kWave, 8 / kW)
 void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                        const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
-                        const float* __restrict__ lse, const float* __restrict__ dvec,
+                        const __bf16* __restrict__ v, const __bf16* __restrict__ o,
+                        const __bf16* __restrict__ dout, const float* __restrict__ lse,
+                        float* __restrict__ dvec,
                         __bf16* __restrict__ dq, int Hq, int Hkv, int N, float c_log2, float scale,
                         int n_qtiles, uint32_t n_xcd) {
   using G = BGeo<D, R>;
@@ -747,7 +718,25 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
   load_rowfrags<D>(df, dout + head_q * D, qrow, n_qrows, hh);
   const int qr = min(qrow, n_qrows - 1);
   const float lse2 = lse[head_q + qr] * kLog2e;
-  const float dd = dvec[head_q + qr];
+  // D of this lane's query row, dO . O in fp32: this lane's half of d
+  // (the dO fragments it holds), then the other half-wave's (lane ^ 32);
+  // written for the dK/dV kernel, which runs after this one
+  float dpart = 0.0f;
+  {
+    const __bf16* po = o + (head_q + qr) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < G::kKSteps; ++s) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(po + 16 * s);
+      const u32x4 b = __builtin_bit_cast(u32x4, df[s]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        dpart = __builtin_fmaf(bf16_bits_to_float(a[w] & 0xFFFFu), bf16_bits_to_float(b[w] & 0xFFFFu), dpart);
+        dpart = __builtin_fmaf(bf16_bits_to_float(a[w] >> 16), bf16_bits_to_float(b[w] >> 16), dpart);
+      }
+    }
+  }
+  const float dd = dpart + __shfl_xor(dpart, 32);
+  if (qvalid && hh == 0) dvec[head_q + qrow] = dd;
 
   f32x16 dqacc[G::kDB];
 #pragma unroll
@@ -815,11 +804,16 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 template <int D>
 hipError_t launch_d(const FwdArgs& a, const BwdArgs& g) {
   const float c_log2 = a.scale * kLog2e;
-  const int64_t n_rows = (int64_t)a.B * a.Hq * a.N;
-  const uint64_t grid0 = ((uint64_t)n_rows * 8 + 255) / 256;
-  hipLaunchKernelGGL((attn_bwd_rowdot_kernel<D>), dim3((uint32_t)grid0), dim3(256), 0, a.stream,
-                     static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(g.dout), g.dvec,
-                     n_rows);
+  // dQ first: it also writes D (the dK/dV kernel's input)
+  constexpr int kDqRows = kDqWaves * kWRows;
+  const int n_qt = (int)(((uint64_t)(a.Hq / a.Hkv) * a.N + kDqRows - 1) / kDqRows);
+  const uint64_t grid2 = (uint64_t)n_qt * a.Hkv * a.B;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, kDqWaves, kDqTRows<D>>), dim3((uint32_t)grid2),
+                     dim3(kDqWaves * kWave), 0, a.stream, static_cast<const __bf16*>(a.q),
+                     static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
+                     static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(g.dout), a.lse,
+                     g.dvec, static_cast<__bf16*>(g.dq), a.Hq, a.Hkv, a.N, c_log2, a.scale, n_qt,
+                     (uint32_t)a.n_xcd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // head dim 128: one wave per 64 keys (attn_bwd_dkdv_w64_kernel); 64: two
@@ -842,16 +836,6 @@ hipError_t launch_d(const FwdArgs& a, const BwdArgs& g) {
                        g.dvec, static_cast<__bf16*>(g.dk), static_cast<__bf16*>(g.dv), a.Hq, a.Hkv,
                        a.N, c_log2, a.scale, n_kt, (uint32_t)a.n_xcd);
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  constexpr int kDqRows = kDqWaves * kWRows;
-  const int n_qt = (int)(((uint64_t)(a.Hq / a.Hkv) * a.N + kDqRows - 1) / kDqRows);
-  const uint64_t grid2 = (uint64_t)n_qt * a.Hkv * a.B;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, kDqWaves, kDqTRows<D>>), dim3((uint32_t)grid2), dim3(kDqWaves * kWave), 0, a.stream,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(g.dout), a.lse,
-                     g.dvec, static_cast<__bf16*>(g.dq), a.Hq, a.Hkv, a.N, c_log2, a.scale, n_qt,
-                     (uint32_t)a.n_xcd);
   return hipGetLastError();
 }
 
